@@ -1,0 +1,203 @@
+"""Benchmark: GPT-2 training steps on one MI355X through libgpt2.so.
+
+A step is zero_grad, k micro-steps of forward + backward (B x T tokens each,
+inputs already resident in HBM), then global-norm clip + AdamW.  Prints one
+JSON line with whole-job tokens/s, ms/step, MFU (6 N + 6 L T C flops per
+token against the bf16 dense MFMA peak), a roofline entry for the dominant
+kernel (timed with HIP events on the stream it runs on) and the CPU oracle's
+throughput on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_124m]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec + MFU, GPT-2 124M bf16 B×T=16×1024, 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--grad-accum", type=int, default=None,
+                    help="override k (micro-steps per optimizer step)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--cpu-sample-batch", type=int, default=1)
+    return ap.parse_args()
+
+
+def time_kernel(fn, stream, iters=20):
+    """Average duration (s) of fn() launches, HIP events on `stream`."""
+    import torch
+    with torch.cuda.stream(stream):
+        fn()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(iters):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / iters
+
+
+def roofline_lm_head(cfg, stream):
+    """bf16 lm_head forward GEMM (M = B*T, N = Vp, K = C): the largest single
+    launch of the step.  Algorithmic flops per launch 2 M N K."""
+    import torch
+    import transformer_lm_pretraining_train_amd as g
+    M, N, K = cfg.micro_batch * cfg.seq_len, cfg.padded_vocab_size, cfg.n_embd
+    ldl = ((N + 63) // 64) * 64
+    with torch.cuda.stream(stream):
+        A = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        B = torch.randn((N, K), device="cuda").to(torch.bfloat16)
+        out = torch.empty((M, ldl), dtype=torch.bfloat16, device="cuda")
+    t = time_kernel(lambda: g.gemm(g.GPT2_BF16, True, True, M, N, K, A, K, B, K, "store", out, ldl,
+                                   stream=stream), stream)
+    flops = 2.0 * M * N * K
+    achieved = flops / t / 1e12
+    return {"kernel": "gemm_mfma_kernel<true,true,EPI_STORE> (lm_head forward, "
+                      f"M={M} N={N} K={K})",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "avg_launch_us": round(t * 1e6, 1)}
+
+
+def cpu_baseline(wl, B_sample):
+    """The CPU oracle (as it stands) on one micro-step of B_sample sequences
+    of the workload plus one AdamW over all parameters; tokens/s."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    ocfg = oracle.Config.from_workload(wl)
+    layout = oracle.param_layout(ocfg)
+    flat = synth.init_params(layout, wl.n_layer, wl.vocab_size, [wl.seed_id, 2])
+    stream = synth.token_stream(wl, B_sample * wl.seq_len + 1)
+    x, y = synth.micro_batch(stream, 0, B_sample, wl.seq_len)
+    m = np.zeros_like(flat)
+    v = np.zeros_like(flat)
+    t0 = time.perf_counter()
+    oracle.train_step(ocfg, flat, m, v, 0, [(x, y)], 6e-4)
+    dt = time.perf_counter() - t0
+    toks = B_sample * wl.seq_len
+    return {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{wl.name}: one micro-step of B={B_sample} x T={wl.seq_len} tokens "
+                      f"(fwd + bwd) plus one clip + AdamW over all parameters, fp32 NumPy; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU data "
+              "parallelism is not part of this build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_lm_pretraining_train_amd as g
+
+    wl = synth.workload(args.workload)
+    if args.grad_accum:
+        wl = wl.replace(grad_accum=args.grad_accum)
+    cfg = g.config_for(wl, "bf16")
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    log(f"bench: {wl.name} bf16, B={wl.micro_batch} T={wl.seq_len} k={wl.grad_accum}")
+
+    with torch.cuda.stream(stream):
+        model = g.Model(cfg, stream=stream)
+        layout = [(n, o, s) for n, o, s, _ in g.param_layout(cfg)]
+        flat = synth.init_params(layout, wl.n_layer, wl.vocab_size, [wl.seed_id, 2])
+        model.set_params(torch.from_numpy(flat).cuda())
+        toks = synth.token_stream(wl, wl.tokens_per_step + 1)
+        batches = []
+        for mi in range(wl.grad_accum):
+            x, y = synth.micro_batch(toks, mi, wl.micro_batch, wl.seq_len)
+            batches.append((torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()))
+        losses = torch.zeros(wl.grad_accum, device="cuda")
+        norm = torch.zeros(1, device="cuda")
+    stream.synchronize()
+
+    def step(s):
+        lr = 6e-4 * min(1.0, s / 700)  # warm-up part of the schedule
+        model.zero_grad()
+        for mi, (x, y) in enumerate(batches):
+            model.forward(x, y, losses[mi:mi + 1])
+            model.backward()
+        model.clip_and_adamw(lr, norm_out=norm)  # waits for the stream
+
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            step(s + 1)
+            log(f"warmup step {s + 1}: loss {losses.mean().item():.4f} norm {norm.item():.4f}")
+        stream.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for s in range(args.steps):
+            step(args.warmup + s + 1)
+        ev1.record(stream)
+        stream.synchronize()
+        wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    log(f"timed {args.steps} steps: wall {wall:.3f} s, events {gpu_s:.3f} s; "
+        f"last loss {losses.mean().item():.4f} norm {norm.item():.4f}")
+    ms = wall / args.steps * 1e3
+    tps = wl.tokens_per_step * args.steps / wall
+    fpt = g.flops_per_token(cfg)
+    mfu = fpt * tps / (PEAK_BF16_TFLOPS * 1e12)
+
+    roof = None
+    if not args.no_roofline:
+        roof = roofline_lm_head(cfg, stream)
+        log(f"roofline: {roof}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl, args.cpu_sample_batch)
+        log(f"cpu baseline: {cpu}")
+    out = {
+        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (Zipf token stream, GPT-2 random init)",
+        "config": {"workload": wl.name, "n_layer": wl.n_layer, "n_head": wl.n_head,
+                   "n_embd": wl.n_embd, "vocab": wl.vocab_size,
+                   "padded_vocab": wl.padded_vocab_size, "micro_batch": wl.micro_batch,
+                   "seq_len": wl.seq_len, "grad_accum": wl.grad_accum,
+                   "tokens_per_step": wl.tokens_per_step, "parallelism": "single-gpu"},
+        "mfu": round(mfu, 4), "flops_per_token": fpt,
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * gpt2.h -- C ABI of libgpt2.so: one GPT-2 pretraining step on one AMD
+ * Instinct MI355X (gfx950), every step in hand-written HIP kernels.
+ *
+ * What is computed (the web pages this method comes from are cited by title
+ * and section):
+ *   - Model: decoder-only GPT-2 -- learned token (wte) and position (wpe)
+ *     embeddings, pre-LayerNorm blocks of causal multi-head self-attention and
+ *     a 4C GELU MLP with residual connections, a final LayerNorm, and an
+ *     output head tied to wte (news post on Karpathy's 4-hour GPT-2 124M
+ *     lecture, rgzn1.com, lecture outline; qntz.me "From 0 to 1 build GPT",
+ *     section on building the Transformer; "Let's reproduce GPT-2 (124M)"
+ *     notes, training-recipe section: weight tying).
+ *   - Loss: mean cross-entropy over B*T positions, vocabulary padded (e.g.
+ *     50257 -> 50304, "Let's reproduce GPT-2 (124M)", GPU optimisation
+ *     ladder, "nice numbers") with the padded logits excluded.
+ *   - Gradient accumulation over k micro-steps with the loss divided by k,
+ *     global gradient-norm clipping, and AdamW with weight decay on 2-D
+ *     tensors only ("Let's reproduce GPT-2 (124M)", training recipe;
+ *     dszhyy.com llm.c 1.5B post, flags section).
+ *   - LayerNorm eps 1e-5 (GPT2Config block on the dszhyy.com page).
+ *
+ * Conventions for every call:
+ *   - Pointers named dev_* are device pointers; everything else is host.
+ *   - Memory is owned by the caller.  The caller allocates one device
+ *     workspace of gpt2_workspace_bytes() bytes and passes it, together
+ *     with a HIP stream, to gpt2_create; the library never allocates or
+ *     frees device memory and never frees caller memory.  gpt2_destroy
+ *     frees only the host handle.
+ *   - Every call enqueues work on the model's stream and returns without
+ *     waiting, except gpt2_clip_and_adamw and gpt2_sync, which wait for the
+ *     stream.  A handle must be used from one host thread at a time.
+ *   - Return value: GPT2_OK (0) or a negative GPT2_E* code; the text of the
+ *     last error on the calling thread is returned by gpt2_last_error().
+ *
+ * Data layout:
+ *   - Parameters form one flat fp32 vector in the order of
+ *     gpt2_param_layout(): wte (Vp, C), wpe (block_size, C), then for each
+ *     layer ln1_w, ln1_b (C), qkv_w (3C, C), qkv_b (3C), proj_w (C, C),
+ *     proj_b (C), ln2_w, ln2_b (C), fc_w (4C, C), fc_b (4C), fcp_w (C, 4C),
+ *     fcp_b (C); last lnf_w, lnf_b (C).  Linear weights are (out, in),
+ *     row-major, applied as y = x W^T + b.  qkv columns are [q | k | v],
+ *     head h at columns h*hd .. (h+1)*hd - 1 within each third.
+ *   - Gradients, AdamW m and v use the same flat layout, fp32.
+ *   - Tokens and targets are int32, row-major (B, T).
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  GPT2_OK = 0,
+  GPT2_EINVAL = -1,      /* bad config, null pointer, or shape mismatch */
+  GPT2_EWORKSPACE = -2,  /* workspace too small or misaligned (256 B) */
+  GPT2_ESTATE = -3,      /* call out of order, e.g. backward before a forward with targets */
+  GPT2_ETOKEN = -4,      /* a token or target id was outside [0, vocab_size) */
+  GPT2_ENONFINITE = -5,  /* gradient norm NaN/Inf: update skipped, state unchanged */
+  GPT2_EHIP = -6         /* a HIP runtime call failed; see gpt2_last_error() */
+};
+
+enum { GPT2_FP32 = 0, GPT2_BF16 = 1 };
+
+typedef struct {
+  int32_t n_layer;
+  int32_t n_head;
+  int32_t n_embd;            /* C; multiple of 64 */
+  int32_t block_size;        /* rows of wpe; seq_len <= block_size */
+  int32_t vocab_size;        /* V: ids in [0, V) */
+  int32_t padded_vocab_size; /* Vp >= V: rows of wte, columns of the logits */
+  int32_t micro_batch;       /* B */
+  int32_t seq_len;           /* T */
+  int32_t grad_accum_steps;  /* k: backward scales the loss by 1/k */
+  int32_t dtype;             /* GPT2_FP32 or GPT2_BF16 (activations + GEMM inputs) */
+  int32_t deterministic;     /* nonzero: no floating-point atomics, bitwise repeatable */
+  float ln_eps;              /* LayerNorm eps, 1e-5 */
+} gpt2_config;
+
+typedef struct {
+  char name[32];     /* e.g. "wte", "h3.qkv_w", "lnf_b" */
+  int64_t offset;    /* element offset in the flat vector */
+  int32_t ndim;      /* 1 or 2 */
+  int32_t decay;     /* 1 if AdamW weight decay applies (2-D tensors) */
+  int64_t shape[2];  /* shape[1] == 1 when ndim == 1 */
+} gpt2_tensor_info;
+
+typedef struct gpt2_model gpt2_model;
+
+/* Bytes of device workspace a model with this config needs (0 if the config
+ * is invalid; the reason is in gpt2_last_error()). */
+size_t gpt2_workspace_bytes(const gpt2_config* cfg);
+
+/* Number of parameters, Vp*C + block_size*C + L*(12C^2 + 13C) + 2C
+ * (wte counted once, lm_head tied).  -1 on an invalid config. */
+int64_t gpt2_num_params(const gpt2_config* cfg);
+
+/* Fills up to cap entries of out with the flat parameter layout and returns
+ * the number of tensors (2 + 12 L + 2), or a negative error code.  out may be
+ * NULL to query the count.  Host only; needs no GPU. */
+int gpt2_param_layout(const gpt2_config* cfg, gpt2_tensor_info* out, int cap);
+
+/* Creates a model over dev_workspace (>= gpt2_workspace_bytes, 256-byte
+ * aligned, owned by the caller, must outlive the model) on the HIP stream
+ * hip_stream (a hipStream_t; NULL = default stream).  Parameters, gradients,
+ * m, v and the step count start at zero.  Synchronous. */
+int gpt2_create(const gpt2_config* cfg, void* dev_workspace, size_t bytes, void* hip_stream,
+                gpt2_model** out);
+int gpt2_destroy(gpt2_model* model);
+
+/* Copy the fp32 flat parameter vector in (also refreshes the bf16 copy used
+ * by the bf16 GEMMs) or out.  dev_* hold gpt2_num_params() floats. */
+int gpt2_set_params(gpt2_model* model, const float* dev_src);
+int gpt2_get_params(gpt2_model* model, float* dev_dst);
+/* Copy the accumulated fp32 gradient vector out or in. */
+int gpt2_get_grads(gpt2_model* model, float* dev_dst);
+int gpt2_set_grads(gpt2_model* model, const float* dev_src);
+/* AdamW state: first and second moments (flat fp32) and the number of
+ * updates applied so far. */
+int gpt2_get_opt_state(gpt2_model* model, float* dev_m, float* dev_v, int64_t* step);
+int gpt2_set_opt_state(gpt2_model* model, const float* dev_m, const float* dev_v, int64_t step);
+
+/* Forward pass on dev_tokens (B, T).  With dev_targets (B, T) non-NULL it
+ * also evaluates the cross-entropy and writes the mean over the B*T
+ * positions (not divided by k) to dev_loss (one float; may be NULL).
+ * Out-of-range ids are clamped for memory safety and reported as
+ * GPT2_ETOKEN by the next gpt2_sync / gpt2_clip_and_adamw. */
+int gpt2_forward(gpt2_model* model, const int32_t* dev_tokens, const int32_t* dev_targets,
+                 float* dev_loss);
+
+/* Backward pass of the last forward (which must have had targets):
+ * gradients += d(mean loss / k) / d params.  Overwrites the logits buffer. */
+int gpt2_backward(gpt2_model* model);
+
+/* Gradients = 0. */
+int gpt2_zero_grad(gpt2_model* model);
+
+/* One optimizer step ("Let's reproduce GPT-2 (124M)", training recipe):
+ * n = ||g||_2 over all gradients; s = min(1, grad_clip / n); g' = s g;
+ * t += 1; m = b1 m + (1-b1) g'; v = b2 v + (1-b2) g'^2;
+ * p -= lr (m/(1-b1^t) / (sqrt(v/(1-b2^t)) + eps) + wd p [2-D tensors]).
+ * Writes n to dev_norm_out (may be NULL).  Waits for the stream; returns
+ * GPT2_ENONFINITE (nothing updated, t unchanged) if n is NaN or Inf, and
+ * GPT2_ETOKEN if an id since the last check was out of range. */
+int gpt2_clip_and_adamw(gpt2_model* model, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, float grad_clip, float* dev_norm_out);
+
+/* Waits for the model's stream and reports pending device-side errors. */
+int gpt2_sync(gpt2_model* model);
+
+/* Debug / test reads of internal buffers (copied on the stream into dev_dst,
+ * which must hold `bytes`).  which = GPT2_DBG_*; layer used by per-layer
+ * buffers.  Element types: LOGITS, ACT_* in the activation dtype (fp32 or
+ * bf16, row pitch listed below); LSE, LOSSES fp32; ARGMAX int32. */
+enum {
+  GPT2_DBG_LOGITS = 0,   /* (B*T, Vp) logits of the last forward, row pitch Vp */
+  GPT2_DBG_LOSSES = 1,   /* (B*T) per-position cross-entropy */
+  GPT2_DBG_ARGMAX = 2,   /* (B*T) argmax over the unpadded vocab, lowest index on ties */
+  GPT2_DBG_ACT_LN1 = 3,  /* (B*T, C) ln1 output of `layer` */
+  GPT2_DBG_ACT_QKV = 4,  /* (B*T, 3C) */
+  GPT2_DBG_ACT_ATTY = 5, /* (B*T, C) attention output before the projection */
+  GPT2_DBG_ACT_RES2 = 6, /* (B*T, C) residual after attention */
+  GPT2_DBG_ACT_FCH = 7,  /* (B*T, 4C) fc pre-activation */
+  GPT2_DBG_ACT_RES3 = 8, /* (B*T, C) residual after the MLP (block output) */
+  GPT2_DBG_ACT_LNF = 9,  /* (B*T, C) final LayerNorm output */
+  GPT2_DBG_ATT_LSE = 10, /* (B, H, T) fp32 log-sum-exp of the scaled scores */
+  GPT2_DBG_ENCODED = 11  /* (B*T, C) wte[tok] + wpe[t] */
+};
+int gpt2_debug_read(gpt2_model* model, int which, int layer, void* dev_dst, size_t bytes);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* gpt2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_H */

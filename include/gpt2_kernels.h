@@ -1,0 +1,68 @@
+/*
+ * gpt2_kernels.h -- kernel-level entry points of libgpt2.so, for unit tests
+ * and micro-benchmarks of the two matrix-core kernels of the GPT-2 step in
+ * isolation.  The training step itself only needs gpt2.h.
+ *
+ * Conventions as in gpt2.h: dev_* are device pointers owned by the caller;
+ * calls enqueue on `hip_stream` (a hipStream_t, NULL = default stream) and
+ * return 0 or a negative GPT2_E* code with the message in
+ * gpt2_last_error().  Element type: dtype GPT2_FP32 -> float,
+ * GPT2_BF16 -> bfloat16 (uint16 storage); bias is always fp32.
+ */
+#ifndef GPT2_KERNELS_H
+#define GPT2_KERNELS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Epilogues of gpt2k_gemm. */
+enum {
+  GPT2K_EPI_STORE = 0,      /* out = acc */
+  GPT2K_EPI_BIAS = 1,       /* out = acc + bias[n] */
+  GPT2K_EPI_BIAS_RESID = 2, /* out = acc + bias[n] + resid[m, n] */
+  GPT2K_EPI_BIAS_GELU = 3,  /* out = acc + bias[n]; out2 = gelu_tanh(out) */
+  GPT2K_EPI_GELU_BWD = 4,   /* out = acc * gelu_tanh'(aux[m, n]) */
+  GPT2K_EPI_ACC_F32 = 5     /* out (always fp32) += acc */
+};
+
+/* C(m, n) = sum_{k < K} A(m, k) B(n, k) for m < M, n < N, then the epilogue,
+ * with fp32 accumulation.  The linear layers of the model are this product
+ * with W stored (out, in): y = x W^T (A, B k-major), dx = dy W (A k-major,
+ * B n-major), dW += dy^T x (A m-major, B n-major) ("Let's reproduce GPT-2
+ * (124M)" notes: the model is built from such matrix multiplies).
+ *   a_kmajor != 0: A(m, k) = A[m*lda + k], else A[k*lda + m];
+ *   b_kmajor != 0: B(n, k) = B[n*ldb + k], else B[k*ldb + n].
+ * Leading dimensions (elements) must be multiples of 8, and each row of A
+ * and B must be readable up to round_up(extent, 8) elements.  Output
+ * leading dimensions ldo, ldr, ldo2, ldx are in elements.  Pointers not used
+ * by the epilogue may be NULL. */
+int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const void* dev_A,
+               int64_t lda, const void* dev_B, int64_t ldb, int epilogue, void* dev_out,
+               int64_t ldo, const float* dev_bias, const void* dev_resid, int64_t ldr,
+               void* dev_out2, int64_t ldo2, const void* dev_aux, int64_t ldx, void* hip_stream);
+
+/* Causal self-attention forward on qkv (B*T, 3C) rows [q | k | v], head h at
+ * columns h*hd within each third, C = H*hd: out (B*T, C) = softmax(q k^T /
+ * sqrt(hd), j <= i) v per head, lse (B, H, T) fp32 = log sum_j exp(scores)
+ * ("Let's reproduce GPT-2 (124M)", GPU optimisation ladder: FlashAttention,
+ * which never stores the T x T matrix). */
+int gpt2k_attention_forward(int dtype, void* dev_out, float* dev_lse, const void* dev_qkv, int B,
+                            int T, int H, int hd, void* hip_stream);
+
+/* Backward of gpt2k_attention_forward: writes dqkv (B*T, 3C) in full from
+ * dout (B*T, C), the forward's qkv, out and lse.  dev_scratch must hold
+ * gpt2k_attention_backward_scratch_bytes(B, T, H) bytes. */
+size_t gpt2k_attention_backward_scratch_bytes(int B, int T, int H);
+int gpt2k_attention_backward(int dtype, void* dev_dqkv, const void* dev_dout, const void* dev_qkv,
+                             const void* dev_out, const float* dev_lse, int B, int T, int H,
+                             int hd, void* dev_scratch, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPT2_KERNELS_H */

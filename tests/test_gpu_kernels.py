@@ -1,0 +1,220 @@
+"""GEMM and attention kernels through the kernel-level C ABI, against the
+oracle's definitions (plain matmul; the oracle's causal attention) on the
+same seeded inputs: small ragged shapes element by element, and the GPT-2
+124M shapes on sampled rows / heads."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import transformer_lm_pretraining_train_amd as g  # noqa: E402
+from gpu_util import bf16_round, cosine, host, rel_l2, to_dev  # noqa: E402
+
+FP32, BF16 = g.GPT2_FP32, g.GPT2_BF16
+
+
+def _store(mat, kmajor, rows, K, ld_extra, rng, pad_value):
+    """Lay out logical operand mat (rows x K) in memory: k-major (rows, ld)
+    or m-major (K, ld).  Padding holds pad_value."""
+    if kmajor:
+        ld = ((K + 7) // 8) * 8 + ld_extra
+        buf = np.full((rows, ld), pad_value, dtype=np.float32)
+        buf[:, :K] = mat
+    else:
+        ld = ((rows + 7) // 8) * 8 + ld_extra
+        buf = np.full((K, ld), pad_value, dtype=np.float32)
+        buf[:, :rows] = mat.T
+    return buf, ld
+
+
+def run_gemm(dt, akm, bkm, M, N, K, epi, seed=0, ld_extra=0, pad_value=np.nan):
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((N, K)).astype(np.float32)
+    if dt == BF16:
+        A, B = bf16_round(A), bf16_round(B)
+    # NaN padding only where the kernel promises not to read it into an
+    # output that is stored: the k tail of k-major operands is masked.
+    Abuf, lda = _store(A, akm, M, K, ld_extra, rng, pad_value if akm else 0.0)
+    Bbuf, ldb = _store(B, bkm, N, K, ld_extra, rng, pad_value if bkm else 0.0)
+    tdt = torch.bfloat16 if dt == BF16 else torch.float32
+    dA, dB = to_dev(Abuf, tdt), to_dev(Bbuf, tdt)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    bias = rng.standard_normal(N).astype(np.float32)
+    resid = rng.standard_normal((M, N)).astype(np.float32)
+    aux = rng.standard_normal((M, N)).astype(np.float32)
+    if dt == BF16:
+        resid, aux = bf16_round(resid), bf16_round(aux)
+    kw = {}
+    if epi == "acc_f32":
+        init = rng.standard_normal((M, N)).astype(np.float32)
+        out = to_dev(init)
+        expect = init + ref
+    else:
+        out = torch.zeros((M, N), dtype=tdt, device="cuda")
+        if epi == "store":
+            expect = ref
+        elif epi == "bias":
+            expect = ref + bias
+        elif epi == "bias_resid":
+            expect = ref + bias + resid
+        elif epi == "bias_gelu":
+            expect = ref + bias
+            out2 = torch.zeros((M, N), dtype=tdt, device="cuda")
+            kw.update(out2=out2, ldo2=N)
+        elif epi == "gelu_bwd":
+            expect = ref * oracle.gelu_grad(aux.astype(np.float64))
+        kw.update(bias=to_dev(bias), resid=to_dev(resid, tdt), ldr=N, aux=to_dev(aux, tdt), ldx=N)
+    g.gemm(dt, akm, bkm, M, N, K, dA, lda, dB, ldb, epi, out, N, **kw)
+    torch.cuda.synchronize()
+    got = host(out)
+    res = {"got": got, "expect": expect}
+    if epi == "bias_gelu":
+        res["got2"] = host(kw["out2"])
+        res["expect2"] = oracle.gelu(got.astype(np.float64))
+    return res
+
+
+ORIENT = [(True, True), (True, False), (False, False), (False, True)]
+EPIS = ["store", "bias", "bias_resid", "bias_gelu", "gelu_bwd", "acc_f32"]
+
+
+@pytest.mark.parametrize("dt", [FP32, BF16])
+@pytest.mark.parametrize("akm,bkm", ORIENT)
+@pytest.mark.parametrize("M,N,K", [(200, 72, 136), (129, 65, 65), (256, 128, 64), (64, 320, 1000)])
+def test_gemm_orientations_ragged(dt, akm, bkm, M, N, K):
+    print(f"gemm dt={dt} akm={akm} bkm={bkm} M={M} N={N} K={K}", flush=True)
+    r = run_gemm(dt, akm, bkm, M, N, K, "store", seed=M + N + K, ld_extra=8)
+    assert np.all(np.isfinite(r["got"]))
+    tol = 1e-5 if dt == FP32 else 4e-3
+    assert rel_l2(r["got"], r["expect"]) < tol
+
+
+@pytest.mark.parametrize("dt", [FP32, BF16])
+@pytest.mark.parametrize("epi", EPIS)
+def test_gemm_epilogues(dt, epi):
+    print(f"gemm epilogue dt={dt} {epi}", flush=True)
+    akm, bkm = (False, False) if epi == "acc_f32" else (True, True)
+    r = run_gemm(dt, akm, bkm, 150, 136, 200, epi, seed=3)
+    tol = 1e-5 if dt == FP32 or epi == "acc_f32" else 4e-3
+    assert rel_l2(r["got"], r["expect"]) < tol
+    if epi == "bias_gelu":
+        assert rel_l2(r["got2"], r["expect2"]) < (1e-5 if dt == FP32 else 4e-3)
+
+
+@pytest.mark.parametrize("akm,bkm,M,N,K", [
+    (True, True, 16384, 2304, 768),     # qkv forward
+    (True, True, 16384, 3072, 768),     # fc forward
+    (True, True, 16384, 768, 3072),     # fc projection forward
+    (True, True, 16384, 50304, 768),    # lm_head forward
+    (True, False, 16384, 768, 50304),   # lm_head input gradient
+    (False, False, 3072, 768, 16384),   # fc weight gradient
+    (False, False, 50304, 768, 16384),  # wte gradient from the head
+])
+def test_gemm_gpt2_124m_shapes_sampled(akm, bkm, M, N, K):
+    """bf16 GEMM at the 124M shapes; 64 sampled output rows against fp64."""
+    print(f"gemm 124M akm={akm} bkm={bkm} M={M} N={N} K={K}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(M ^ N ^ K)
+    A = torch.randn((M, K) if akm else (K, M), device="cuda", generator=gen).to(torch.bfloat16)
+    B = torch.randn((N, K) if bkm else (K, N), device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    g.gemm(BF16, akm, bkm, M, N, K, A, A.shape[1], B, B.shape[1], "store", out, N)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(M ^ N ^ K).choice(M, 64, replace=False)
+    ridx = torch.from_numpy(rows).cuda()
+    Am = (A[ridx] if akm else A[:, ridx].T).float().cpu().numpy().astype(np.float64)
+    Bm = (B if bkm else B.T).float().cpu().numpy().astype(np.float64)
+    ref = Am @ Bm.T
+    got = out[ridx].float().cpu().numpy()
+    assert rel_l2(got, ref) < 4e-3
+
+
+# ------------------------------------------------------------------ attention
+def attention_case(dt, B, T, H, hd, seed):
+    rng = np.random.default_rng(seed)
+    C = H * hd
+    qkv = rng.standard_normal((B * T, 3 * C)).astype(np.float32)
+    dout = rng.standard_normal((B * T, C)).astype(np.float32)
+    if dt == BF16:
+        qkv, dout = bf16_round(qkv), bf16_round(dout)
+    tdt = torch.bfloat16 if dt == BF16 else torch.float32
+    d_qkv = to_dev(qkv, tdt)
+    d_out = torch.empty((B * T, C), dtype=tdt, device="cuda")
+    d_lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    g.attention_forward(dt, d_out, d_lse, d_qkv, B, T, H, hd)
+    d_dout = to_dev(dout, tdt)
+    d_dqkv = torch.full((B * T, 3 * C), float("nan"), dtype=tdt, device="cuda")
+    scratch = torch.empty(g.attention_backward_scratch_bytes(B, T, H), dtype=torch.uint8,
+                          device="cuda")
+    g.attention_backward(dt, d_dqkv, d_dout, d_qkv, d_out, d_lse, B, T, H, hd, scratch)
+    torch.cuda.synchronize()
+    return qkv, dout, host(d_out), host(d_lse), host(d_dqkv)
+
+
+def oracle_attention(qkv, dout, B, T, H):
+    q, k, v = oracle.split_heads(qkv.astype(np.float64), B, T, H)
+    o, p = oracle.causal_attention_forward(q, k, v)
+    do = dout.astype(np.float64).reshape(B, T, H, -1).transpose(0, 2, 1, 3)
+    dq, dk, dv = oracle.causal_attention_backward(do, q, k, v, p)
+    dqkv = np.concatenate([oracle.merge_heads(dq), oracle.merge_heads(dk), oracle.merge_heads(dv)], 1)
+    hd = q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(hd)
+    s = np.where(np.triu(np.ones((T, T), bool), 1), -np.inf, s)
+    mx = s.max(-1, keepdims=True)
+    lse = (mx + np.log(np.exp(s - mx).sum(-1, keepdims=True)))[..., 0]
+    return oracle.merge_heads(o), lse, dqkv
+
+
+@pytest.mark.parametrize("dt", [FP32, BF16])
+@pytest.mark.parametrize("B,T,H,hd", [(2, 100, 3, 64), (3, 64, 4, 16), (1, 1, 2, 64), (2, 130, 2, 16),
+                                      (1, 257, 2, 64)])
+def test_attention_matches_oracle(dt, B, T, H, hd):
+    print(f"attention dt={dt} B={B} T={T} H={H} hd={hd}", flush=True)
+    qkv, dout, out, lse, dqkv = attention_case(dt, B, T, H, hd, seed=T + hd)
+    ro, rlse, rdqkv = oracle_attention(qkv, dout, B, T, H)
+    if dt == FP32:
+        assert rel_l2(out, ro) < 1e-5
+        assert np.max(np.abs(lse - rlse)) < 1e-4
+        assert rel_l2(dqkv, rdqkv) < 1e-4
+    else:
+        assert rel_l2(out, ro) < 1e-2
+        assert np.max(np.abs(lse - rlse)) < 2e-2
+        C = H * hd
+        for part in range(3):
+            sl = slice(part * C, (part + 1) * C)
+            assert cosine(dqkv[:, sl], rdqkv[:, sl]) > 0.999
+            assert rel_l2(dqkv[:, sl], rdqkv[:, sl]) < 3e-2
+
+
+def test_attention_t1_returns_v():
+    """With one position the output is v and lse is the single score."""
+    qkv, dout, out, lse, dqkv = attention_case(FP32, 3, 1, 2, 64, seed=5)
+    C = 128
+    assert np.allclose(out, qkv[:, 2 * C:], rtol=1e-6, atol=1e-6)
+    assert np.all(dqkv[:, :2 * C] == 0)  # dq = dk = 0: softmax over one element
+    assert np.allclose(dqkv[:, 2 * C:], dout, rtol=1e-6)
+
+
+def test_attention_gpt2_124m_sampled_heads():
+    """bf16 at B=16, T=1024, H=12, hd=64; two (b, h) slices vs the oracle."""
+    B, T, H, hd = 16, 1024, 12, 64
+    print(f"attention 124M bf16 B={B} T={T} H={H}", flush=True)
+    qkv, dout, out, lse, dqkv = attention_case(BF16, B, T, H, hd, seed=11)
+    C = H * hd
+    for b, h in [(0, 0), (13, 7)]:
+        rows = slice(b * T, (b + 1) * T)
+        cols = np.r_[h * hd:(h + 1) * hd, C + h * hd:C + (h + 1) * hd,
+                     2 * C + h * hd:2 * C + (h + 1) * hd]
+        sub = qkv[rows][:, cols]
+        ro, rlse, rd = oracle_attention(sub, dout[rows][:, h * hd:(h + 1) * hd], 1, T, 1)
+        assert rel_l2(out[rows][:, h * hd:(h + 1) * hd], ro) < 1e-2
+        assert np.max(np.abs(lse[b, h] - rlse[0, 0])) < 2e-2
+        got = dqkv[rows][:, cols]
+        for part in range(3):
+            sl = slice(part * hd, (part + 1) * hd)
+            assert cosine(got[:, sl], rd[:, sl]) > 0.999

@@ -1,0 +1,79 @@
+// Shared device helpers for the gfx950 kernels: element types, 16-byte
+// packs, wave64 reductions, fast transcendentals.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+
+#define GPT2_WAVE 64
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <class T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }  // RNE
+
+// ---------------------------------------------------------------- 16-byte packs
+// One 16-byte vector of T: 4 floats or 8 bf16.
+template <class T> struct Pack {
+  static constexpr int N = 16 / sizeof(T);
+  union {
+    uint4 u;
+    T e[N];
+  };
+};
+
+template <class T> __device__ __forceinline__ Pack<T> load_pack(const T* p) {
+  Pack<T> r;
+  r.u = *reinterpret_cast<const uint4*>(p);
+  return r;
+}
+template <class T> __device__ __forceinline__ void store_pack(T* p, const Pack<T>& v) {
+  *reinterpret_cast<uint4*>(p) = v.u;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- math
+// exp(x) via the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// tanh(u) = 1 - 2 / (exp(2u) + 1); saturates correctly at +-inf.
+__device__ __forceinline__ float tanh_from_exp(float u) {
+  float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // exp(2u)
+  return 1.0f - 2.0f / (e + 1.0f);
+}
+
+// GELU, tanh form: 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))).
+__device__ __forceinline__ float gelu_f(float h) {
+  const float k = 0.7978845608028654f;
+  float t = tanh_from_exp(k * (h + 0.044715f * h * h * h));
+  return 0.5f * h * (1.0f + t);
+}
+// d gelu / d h for the tanh form.
+__device__ __forceinline__ float gelu_grad_f(float h) {
+  const float k = 0.7978845608028654f;
+  float t = tanh_from_exp(k * (h + 0.044715f * h * h * h));
+  return 0.5f * (1.0f + t) + 0.5f * h * (1.0f - t * t) * k * (1.0f + 3.0f * 0.044715f * h * h);
+}
+
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }

@@ -1,0 +1,657 @@
+// Memory-bound kernels of the GPT-2 step for gfx950: embedding gather and
+// scatter, LayerNorm forward/backward, bias gradients, the masked softmax
+// cross-entropy over the padded vocabulary, and the optimizer (global norm,
+// clip, AdamW), plus fills and casts.
+//
+// All of them stream rows with 16-byte accesses and reduce within a wave64
+// (shuffles) or a workgroup (LDS); column reductions (LayerNorm gain/shift
+// and bias gradients) are two-stage with partials in a scratch buffer and a
+// fixed summation order, so they are bitwise repeatable.
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+
+// 8 consecutive elements <-> floats
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16* p, float v[8]) {
+  Pack<bf16> a = load_pack(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = to_f(a.e[i]);
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(bf16* p, const float v[8]) {
+  Pack<bf16> a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a.e[i] = from_f<bf16>(v[i]);
+  store_pack(p, a);
+}
+
+#define DISPATCH_DT(dt, ...)                 \
+  do {                                       \
+    if ((dt) == BF16) {                      \
+      typedef bf16 T;                        \
+      __VA_ARGS__;                           \
+    } else {                                 \
+      typedef float T;                       \
+      __VA_ARGS__;                           \
+    }                                        \
+  } while (0)
+
+static inline int grid_for(int64_t n, int block) { return (int)cdiv(n, block); }
+
+// =========================================================== embedding
+// x0[m, c] = wte[tok[m], c] + wpe[m % T, c]; one thread per 8 channels.
+template <class T>
+__global__ void encoder_fwd_kernel(T* __restrict__ out, const int32_t* __restrict__ tok,
+                                   const float* __restrict__ wte, const float* __restrict__ wpe,
+                                   int M, int Tn, int C, int V, int* __restrict__ flag) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int cpr = C / 8;
+  if (idx >= (int64_t)M * cpr) return;
+  int m = (int)(idx / cpr);
+  int c = (int)(idx % cpr) * 8;
+  int t = m % Tn;
+  int id = tok[m];
+  if (id < 0 || id >= V) {
+    if (c == 0) atomicOr(flag, 1);
+    id = id < 0 ? 0 : V - 1;
+  }
+  float a[8], b[8];
+  load8(wte + (int64_t)id * C + c, a);
+  load8(wpe + (int64_t)t * C + c, b);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] += b[i];
+  store8(out + (int64_t)m * C + c, a);
+}
+
+hipError_t encoder_forward(int dt, void* out, const int32_t* tok, const float* wte,
+                           const float* wpe, int M, int Tn, int C, int V, int* err_flag,
+                           hipStream_t s) {
+  int64_t n = (int64_t)M * (C / 8);
+  DISPATCH_DT(dt, encoder_fwd_kernel<T><<<grid_for(n, 256), 256, 0, s>>>(
+                      (T*)out, tok, wte, wpe, M, Tn, C, V, err_flag));
+  return hipGetLastError();
+}
+
+// dwpe[t, c] += sum_b dx[b*T + t, c]; one thread per 8 channels of one t.
+template <class T>
+__global__ void encoder_bwd_wpe_kernel(float* __restrict__ dwpe, const T* __restrict__ dx, int B,
+                                       int Tn, int C) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int cpr = C / 8;
+  if (idx >= (int64_t)Tn * cpr) return;
+  int t = (int)(idx / cpr);
+  int c = (int)(idx % cpr) * 8;
+  float acc[8], v[8];
+  load8(dwpe + (int64_t)t * C + c, acc);
+  for (int b = 0; b < B; ++b) {
+    load8(dx + ((int64_t)b * Tn + t) * C + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  store8(dwpe + (int64_t)t * C + c, acc);
+}
+
+hipError_t encoder_backward_wpe(int dt, float* dwpe, const void* dx, int B, int Tn, int C,
+                                hipStream_t s) {
+  int64_t n = (int64_t)Tn * (C / 8);
+  DISPATCH_DT(dt, encoder_bwd_wpe_kernel<T><<<grid_for(n, 256), 256, 0, s>>>(
+                      dwpe, (const T*)dx, B, Tn, C));
+  return hipGetLastError();
+}
+
+// dwte[tok[m], c] += dx[m, c]: fp32 atomics (tokens collide under Zipf).
+template <class T>
+__global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, const T* __restrict__ dx,
+                                       const int32_t* __restrict__ tok, int M, int C, int V) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int cpr = C / 8;
+  if (idx >= (int64_t)M * cpr) return;
+  int m = (int)(idx / cpr);
+  int c = (int)(idx % cpr) * 8;
+  int id = tok[m];
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+  float v[8];
+  load8(dx + (int64_t)m * C + c, v);
+  float* dst = dwte + (int64_t)id * C + c;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unsafeAtomicAdd(dst + i, v[i]);
+}
+
+hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32_t* tok, int M,
+                                int C, int V, hipStream_t s) {
+  int64_t n = (int64_t)M * (C / 8);
+  DISPATCH_DT(dt, encoder_bwd_wte_kernel<T><<<grid_for(n, 256), 256, 0, s>>>(
+                      dwte, (const T*)dx, tok, M, C, V));
+  return hipGetLastError();
+}
+
+// =========================================================== LayerNorm
+// One wave per row; lane j owns 8-element chunks j, j+64, ... (C % 8 == 0).
+constexpr int LN_MAXCH = 4;  // C <= 8 * 64 * 4 = 2048
+
+template <class T>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(
+    T* __restrict__ out, float* __restrict__ mean_out, float* __restrict__ rstd_out,
+    const T* __restrict__ inp, const float* __restrict__ w, const float* __restrict__ b, int M,
+    int C, float eps) {
+  int row = blockIdx.x * 4 + threadIdx.x / 64;
+  int lane = threadIdx.x % 64;
+  if (row >= M) return;
+  int nch = C / 8;
+  const T* x = inp + (int64_t)row * C;
+  float v[LN_MAXCH][8];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < LN_MAXCH; ++j) {
+    int ch = lane + 64 * j;
+    if (ch < nch) {
+      load8(x + ch * 8, v[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[j][i];
+    }
+  }
+  float mean = wave_sum(s) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < LN_MAXCH; ++j) {
+    int ch = lane + 64 * j;
+    if (ch < nch) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float d = v[j][i] - mean;
+        ss += d * d;
+      }
+    }
+  }
+  float var = wave_sum(ss) / C;
+  float rstd = 1.0f / sqrtf(var + eps);
+  T* y = out + (int64_t)row * C;
+#pragma unroll
+  for (int j = 0; j < LN_MAXCH; ++j) {
+    int ch = lane + 64 * j;
+    if (ch < nch) {
+      float wv[8], bv[8], o[8];
+      load8(w + ch * 8, wv);
+      load8(b + ch * 8, bv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = (v[j][i] - mean) * rstd * wv[i] + bv[i];
+      store8(y + ch * 8, o);
+    }
+  }
+  if (lane == 0) {
+    mean_out[row] = mean;
+    rstd_out[row] = rstd;
+  }
+}
+
+hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,
+                             const float* w, const float* b, int M, int C, float eps,
+                             hipStream_t s) {
+  if (C % 8 != 0 || C > 8 * 64 * LN_MAXCH) return hipErrorInvalidValue;
+  DISPATCH_DT(dt, layernorm_fwd_kernel<T><<<grid_for(M, 4), 256, 0, s>>>(
+                      (T*)out, mean, rstd, (const T*)inp, w, b, M, C, eps));
+  return hipGetLastError();
+}
+
+// Backward: per row, g = dy * w, xhat = (x - mean) rstd,
+// dx = rstd (g - mean(g) - xhat mean(g xhat)); dres += dx.
+// Each workgroup handles LNB_ROWS rows and writes partial column sums of
+// dy*xhat and dy to scratch[block][2][C]; a second kernel adds them up.
+constexpr int LNB_ROWS = 32;
+
+template <class T>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(
+    T* __restrict__ dres, float* __restrict__ partial, const T* __restrict__ dy,
+    const T* __restrict__ inp, const float* __restrict__ mean, const float* __restrict__ rstd,
+    const float* __restrict__ w, int M, int C) {
+  extern __shared__ float red[];  // [2][C]
+  int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  int nch = C / 8;
+  float dwacc[LN_MAXCH][8], dbacc[LN_MAXCH][8];
+#pragma unroll
+  for (int j = 0; j < LN_MAXCH; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dwacc[j][i] = dbacc[j][i] = 0.f;
+
+  int row0 = blockIdx.x * LNB_ROWS;
+  for (int r = wave; r < LNB_ROWS; r += 4) {
+    int row = row0 + r;
+    if (row >= M) break;
+    float mu = mean[row], rs = rstd[row];
+    const T* x = inp + (int64_t)row * C;
+    const T* g = dy + (int64_t)row * C;
+    float xh[LN_MAXCH][8], gw[LN_MAXCH][8];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < LN_MAXCH; ++j) {
+      int ch = lane + 64 * j;
+      if (ch < nch) {
+        float xv[8], gv[8], wv[8];
+        load8(x + ch * 8, xv);
+        load8(g + ch * 8, gv);
+        load8(w + ch * 8, wv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          xh[j][i] = (xv[i] - mu) * rs;
+          gw[j][i] = gv[i] * wv[i];
+          s1 += gw[j][i];
+          s2 += gw[j][i] * xh[j][i];
+          dwacc[j][i] += gv[i] * xh[j][i];
+          dbacc[j][i] += gv[i];
+        }
+      }
+    }
+    s1 = wave_sum(s1) / C;
+    s2 = wave_sum(s2) / C;
+    T* d = dres + (int64_t)row * C;
+#pragma unroll
+    for (int j = 0; j < LN_MAXCH; ++j) {
+      int ch = lane + 64 * j;
+      if (ch < nch) {
+        float dv[8];
+        load8(d + ch * 8, dv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dv[i] += rs * (gw[j][i] - s1 - xh[j][i] * s2);
+        store8(d + ch * 8, dv);
+      }
+    }
+  }
+  // fixed-order reduction of the four waves' column sums
+  for (int wv = 0; wv < 4; ++wv) {
+    if (wave == wv) {
+#pragma unroll
+      for (int j = 0; j < LN_MAXCH; ++j) {
+        int ch = lane + 64 * j;
+        if (ch < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            int c = ch * 8 + i;
+            if (wv == 0) {
+              red[c] = dwacc[j][i];
+              red[C + c] = dbacc[j][i];
+            } else {
+              red[c] += dwacc[j][i];
+              red[C + c] += dbacc[j][i];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* dst = partial + (int64_t)blockIdx.x * 2 * C;
+  for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) dst[c] = red[c];
+}
+
+// out[c] += sum_b partial[b][c] over nb blocks, c < n (fixed order).
+__global__ void column_partials_reduce_kernel(float* __restrict__ out0, float* __restrict__ out1,
+                                              const float* __restrict__ partial, int nb, int C,
+                                              int stride) {
+  int c = blockIdx.x * blockDim.x + threadIdx.x;
+  int total = out1 ? 2 * C : C;
+  if (c >= total) return;
+  float acc = 0.f;
+  for (int b = 0; b < nb; ++b) acc += partial[(int64_t)b * stride + c];
+  if (c < C)
+    out0[c] += acc;
+  else
+    out1[c - C] += acc;
+}
+
+size_t layernorm_backward_scratch_bytes(int M, int C) {
+  return (size_t)cdiv(M, LNB_ROWS) * 2 * C * sizeof(float);
+}
+
+hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, const void* dy,
+                              const void* inp, const float* mean, const float* rstd,
+                              const float* w, int M, int C, void* scratch, hipStream_t s) {
+  if (C % 8 != 0 || C > 8 * 64 * LN_MAXCH) return hipErrorInvalidValue;
+  int nb = (int)cdiv(M, LNB_ROWS);
+  float* partial = (float*)scratch;
+  DISPATCH_DT(dt, layernorm_bwd_kernel<T><<<nb, 256, 2 * C * sizeof(float), s>>>(
+                      (T*)dres, partial, (const T*)dy, (const T*)inp, mean, rstd, w, M, C));
+  column_partials_reduce_kernel<<<grid_for(2 * C, 256), 256, 0, s>>>(dw, db, partial, nb, C,
+                                                                      2 * C);
+  return hipGetLastError();
+}
+
+// =========================================================== bias gradient
+// Workgroup: 32 column chunks of 8 (256 columns) x 8 row lanes, over a
+// chunk of BG_ROWS rows; partial[rowchunk][N].
+constexpr int BG_ROWS = 256;
+
+template <class T>
+__global__ __launch_bounds__(256) void bias_grad_kernel(float* __restrict__ partial,
+                                                        const T* __restrict__ dy, int M, int N,
+                                                        int64_t ldy) {
+  __shared__ float red[8][256 + 4];
+  int cc = threadIdx.x % 32, rl = threadIdx.x / 32;
+  int col = blockIdx.x * 256 + cc * 8;
+  int row0 = blockIdx.y * BG_ROWS;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col < N) {
+    int rend = min(row0 + BG_ROWS, M);
+    for (int r = row0 + rl; r < rend; r += 8) {
+      float v[8];
+      load8(dy + (int64_t)r * ldy + col, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cc * 8 + i] = acc[i];
+  __syncthreads();
+  int c = threadIdx.x;  // 256 columns of this workgroup
+  if (blockIdx.x * 256 + c < N) {
+    float t = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t += red[r][c];
+    partial[(int64_t)blockIdx.y * N + blockIdx.x * 256 + c] = t;
+  }
+}
+
+size_t bias_grad_scratch_bytes(int M, int N) {
+  return (size_t)cdiv(M, BG_ROWS) * N * sizeof(float);
+}
+
+hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ldy, void* scratch,
+                     hipStream_t s) {
+  if (N % 8 != 0 || ldy % 8 != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)cdiv(N, 256), (unsigned)cdiv(M, BG_ROWS));
+  float* partial = (float*)scratch;
+  DISPATCH_DT(dt, bias_grad_kernel<T><<<grid, 256, 0, s>>>(partial, (const T*)dy, M, N, ldy));
+  column_partials_reduce_kernel<<<grid_for(N, 256), 256, 0, s>>>(db, nullptr, partial,
+                                                                  (int)grid.y, N, N);
+  return hipGetLastError();
+}
+
+// =========================================================== cross-entropy
+// One workgroup per row: online max / sum-exp / argmax over columns < V.
+struct SoftmaxState {
+  float m;  // running max
+  float s;  // sum of exp(z - m)
+  int arg;  // lowest index attaining m
+};
+
+__device__ __forceinline__ SoftmaxState sm_combine(SoftmaxState a, SoftmaxState b) {
+  SoftmaxState r;
+  if (a.m > b.m || (a.m == b.m && a.arg < b.arg)) {
+    r.m = a.m;
+    r.arg = a.arg;
+  } else {
+    r.m = b.m;
+    r.arg = b.arg;
+  }
+  float sa = a.s == 0.f ? 0.f : a.s * fast_exp(a.m - r.m);
+  float sb = b.s == 0.f ? 0.f : b.s * fast_exp(b.m - r.m);
+  r.s = sa + sb;
+  return r;
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void ce_fwd_kernel(float* __restrict__ losses,
+                                                     float* __restrict__ lse_out,
+                                                     int32_t* __restrict__ argmax_out,
+                                                     const T* __restrict__ logits, int64_t ldl,
+                                                     const int32_t* __restrict__ targets, int V,
+                                                     int* __restrict__ flag) {
+  __shared__ SoftmaxState part[4];
+  int row = blockIdx.x;
+  const T* z = logits + (int64_t)row * ldl;
+  SoftmaxState st = {-INFINITY, 0.f, 0x7fffffff};
+  for (int c0 = threadIdx.x * 8; c0 < V; c0 += 256 * 8) {
+    float v[8];
+    load8(z + c0, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int c = c0 + i;
+      if (c < V) {
+        float x = v[i];
+        if (x > st.m) {
+          st.s = st.s * fast_exp(st.m - x) + 1.f;
+          st.m = x;
+          st.arg = c;
+        } else {
+          st.s += fast_exp(x - st.m);
+        }
+      }
+    }
+  }
+  // wave reduction
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    SoftmaxState t;
+    t.m = __shfl_xor(st.m, o, 64);
+    t.s = __shfl_xor(st.s, o, 64);
+    t.arg = __shfl_xor(st.arg, o, 64);
+    st = sm_combine(st, t);
+  }
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    SoftmaxState r = part[0];
+    for (int w = 1; w < 4; ++w) r = sm_combine(r, part[w]);
+    float lse = r.m + logf(r.s);
+    int y = targets[row];
+    if (y < 0 || y >= V) {
+      atomicOr(flag, 2);
+      y = y < 0 ? 0 : V - 1;
+    }
+    losses[row] = lse - to_f(z[y]);
+    lse_out[row] = lse;
+    argmax_out[row] = r.arg;
+  }
+}
+
+hipError_t crossentropy_forward(int dt, float* losses, float* lse, int32_t* argmax,
+                                const void* logits, int64_t ldl, const int32_t* targets, int M,
+                                int V, int* err_flag, hipStream_t s) {
+  if (ldl % 8 != 0 || ldl < V) return hipErrorInvalidValue;
+  DISPATCH_DT(dt, ce_fwd_kernel<T><<<M, 256, 0, s>>>(losses, lse, argmax, (const T*)logits, ldl,
+                                                     targets, V, err_flag));
+  return hipGetLastError();
+}
+
+// mean of M per-row losses, one workgroup, fixed order.
+__global__ __launch_bounds__(256) void mean_loss_kernel(float* __restrict__ out,
+                                                        const float* __restrict__ losses, int M) {
+  __shared__ double part[4];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < M; i += 256) acc += losses[i];
+  acc = wave_sum_d(acc);
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = (float)((part[0] + part[1] + part[2] + part[3]) / M);
+}
+
+hipError_t mean_loss(float* out, const float* losses, int M, hipStream_t s) {
+  mean_loss_kernel<<<1, 256, 0, s>>>(out, losses, M);
+  return hipGetLastError();
+}
+
+// dz = seed * (exp(z - lse) - [c == y]) for c < V, 0 for V <= c < ldl.
+template <class T>
+__global__ void ce_bwd_kernel(T* __restrict__ logits, int64_t ldl, const float* __restrict__ lse,
+                              const int32_t* __restrict__ targets, int M, int V, float seed) {
+  int64_t cpr = ldl / 8;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * cpr) return;
+  int row = (int)(idx / cpr);
+  int c0 = (int)(idx % cpr) * 8;
+  T* z = logits + (int64_t)row * ldl + c0;
+  float l = lse[row];
+  int y = targets[row];
+  float v[8];
+  load8(z, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int c = c0 + i;
+    float p = c < V ? fast_exp(v[i] - l) : 0.f;
+    if (c == y) p -= 1.f;
+    v[i] = p * seed;
+  }
+  store8(z, v);
+}
+
+hipError_t crossentropy_backward(int dt, void* logits, int64_t ldl, const float* lse,
+                                 const int32_t* targets, int M, int V, float seed, hipStream_t s) {
+  if (ldl % 8 != 0) return hipErrorInvalidValue;
+  int64_t n = (int64_t)M * (ldl / 8);
+  DISPATCH_DT(dt, ce_bwd_kernel<T><<<grid_for(n, 256), 256, 0, s>>>((T*)logits, ldl, lse, targets,
+                                                                    M, V, seed));
+  return hipGetLastError();
+}
+
+// =========================================================== optimizer
+constexpr int NORM_BLOCKS = 1024;
+
+struct NormScratch {
+  double partial[NORM_BLOCKS];
+  float result[2];  // norm, clip scale
+};
+
+size_t grad_norm_scratch_bytes() { return sizeof(NormScratch); }
+const float* grad_norm_result(const void* scratch) {
+  return reinterpret_cast<const NormScratch*>(scratch)->result;
+}
+
+__global__ __launch_bounds__(256) void sumsq_kernel(double* __restrict__ partial,
+                                                    const float* __restrict__ g, int64_t n) {
+  __shared__ double part[4];
+  double acc = 0.0;
+  int64_t n4 = n / 4;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 v = g4[i];
+    acc += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += 256) acc += (double)g[i] * g[i];
+  acc = wave_sum_d(acc);
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+__global__ __launch_bounds__(256) void norm_finish_kernel(NormScratch* __restrict__ sc,
+                                                          float clip, float* __restrict__ norm_out) {
+  __shared__ double part[4];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < NORM_BLOCKS; i += 256) acc += sc->partial[i];
+  acc = wave_sum_d(acc);
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double nrm = sqrt(part[0] + part[1] + part[2] + part[3]);
+    float nf = (float)nrm;
+    float scale = (nrm > (double)clip) ? (float)((double)clip / nrm) : 1.0f;
+    sc->result[0] = nf;
+    sc->result[1] = scale;
+    if (norm_out) *norm_out = nf;
+  }
+}
+
+hipError_t grad_norm(const float* g, int64_t n, float clip, void* scratch, float* norm_out,
+                     hipStream_t s) {
+  NormScratch* sc = (NormScratch*)scratch;
+  sumsq_kernel<<<NORM_BLOCKS, 256, 0, s>>>(sc->partial, g, n);
+  norm_finish_kernel<<<1, 256, 0, s>>>(sc, clip, norm_out);
+  return hipGetLastError();
+}
+
+__device__ __forceinline__ bool decays(int64_t i, const DecayMap& d) {
+  if (i < d.layer0) return true;  // wte, wpe
+  if (i >= d.n_layer_end) return false;  // final LayerNorm
+  int64_t r = (i - d.layer0) % d.layer_size;
+  return (r >= d.qkvw0 && r < d.qkvw1) || (r >= d.projw0 && r < d.projw1) ||
+         (r >= d.fcw0 && r < d.fcw1) || (r >= d.fcpw0 && r < d.fcpw1);
+}
+
+// One thread per 4 elements (tensor boundaries are multiples of C, C % 64 == 0,
+// so a group of 4 never straddles two tensors).  Skips everything when the
+// norm is not finite.
+__global__ __launch_bounds__(256) void adamw_kernel(
+    float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
+    float* __restrict__ v, bf16* __restrict__ shadow, int64_t n, float lr, float b1, float b2,
+    float eps, float wd, float bc1, float bc2, const float* __restrict__ norm_scale, DecayMap dm) {
+  float nrm = norm_scale[0];
+  if (!isfinite(nrm)) return;
+  float scale = norm_scale[1];
+  int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  float dec = decays(i4, dm) ? wd : 0.f;
+  int cnt = (int)min((int64_t)4, n - i4);
+  for (int j = 0; j < cnt; ++j) {
+    int64_t i = i4 + j;
+    float gi = g[i] * scale;
+    float mi = b1 * m[i] + (1.f - b1) * gi;
+    float vi = b2 * v[i] + (1.f - b2) * gi * gi;
+    m[i] = mi;
+    v[i] = vi;
+    float mhat = mi / bc1;
+    float vhat = vi / bc2;
+    float pi = p[i];
+    pi -= lr * (mhat / (sqrtf(vhat) + eps) + dec * pi);
+    p[i] = pi;
+    if (shadow) shadow[i] = (bf16)pi;
+  }
+}
+
+hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n, float lr,
+                 float b1, float b2, float eps, float wd, float bc1, float bc2,
+                 const float* norm_scale, DecayMap dm, hipStream_t s) {
+  int64_t threads = cdiv(n, 4);
+  adamw_kernel<<<grid_for(threads, 256), 256, 0, s>>>(p, g, m, v, (bf16*)shadow, n, lr, b1, b2,
+                                                      eps, wd, bc1, bc2, norm_scale, dm);
+  return hipGetLastError();
+}
+
+// =========================================================== fills / casts
+__global__ void fill_f32_kernel(float* __restrict__ p, float value, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t value, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+__global__ void cast_bf16_kernel(bf16* __restrict__ dst, const float* __restrict__ src, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = (bf16)src[i];
+}
+
+static inline int stride_grid(int64_t n) {
+  int64_t g = cdiv(n, 256);
+  return (int)(g < 8192 ? g : 8192);
+}
+
+hipError_t fill_f32(float* p, float value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_f32_kernel<<<stride_grid(n), 256, 0, s>>>(p, value, n);
+  return hipGetLastError();
+}
+hipError_t fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<stride_grid(n), 256, 0, s>>>(p, value, n);
+  return hipGetLastError();
+}
+hipError_t cast_f32_to_bf16(void* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  cast_bf16_kernel<<<stride_grid(n), 256, 0, s>>>((bf16*)dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace gk

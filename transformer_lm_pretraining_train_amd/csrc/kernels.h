@@ -1,0 +1,102 @@
+// Host-side launchers for the gfx950 kernels.  Pointers are device
+// pointers; `dt` selects the activation element type (0 = fp32, 1 = bf16).
+// Every launcher enqueues on `s` and returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+inline size_t dsize(int dt) { return dt == BF16 ? 2 : 4; }
+
+// ---- embedding
+hipError_t encoder_forward(int dt, void* out, const int32_t* tok, const float* wte, const float* wpe,
+                           int M, int T, int C, int V, int* err_flag, hipStream_t s);
+hipError_t encoder_backward_wpe(int dt, float* dwpe, const void* dx, int B, int T, int C,
+                                hipStream_t s);
+// dwte[tok[m]] += dx[m] with fp32 atomics (ids clamped to [0, V)).
+hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32_t* tok, int M,
+                                int C, int V, hipStream_t s);
+
+// ---- LayerNorm
+hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,
+                             const float* w, const float* b, int M, int C, float eps, hipStream_t s);
+// dres += dx; dw, db += column sums (two-stage, partials in scratch).
+size_t layernorm_backward_scratch_bytes(int M, int C);
+hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, const void* dy,
+                              const void* inp, const float* mean, const float* rstd, const float* w,
+                              int M, int C, void* scratch, hipStream_t s);
+
+// ---- bias gradient: db[n] += sum_m dy[m, n] (two-stage, partials in scratch)
+size_t bias_grad_scratch_bytes(int M, int N);
+hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ldy, void* scratch,
+                     hipStream_t s);
+
+// ---- cross-entropy over the padded vocabulary (row pitch ldl >= Vp)
+hipError_t crossentropy_forward(int dt, float* losses, float* lse, int32_t* argmax,
+                                const void* logits, int64_t ldl, const int32_t* targets, int M,
+                                int V, int* err_flag, hipStream_t s);
+hipError_t mean_loss(float* out, const float* losses, int M, hipStream_t s);
+// in place: logits <- seed * (softmax - onehot) for columns < V, 0 for V..ldl-1
+hipError_t crossentropy_backward(int dt, void* logits, int64_t ldl, const float* lse,
+                                 const int32_t* targets, int M, int V, float seed, hipStream_t s);
+
+// ---- attention (qkv rows of 3C: [q | k | v], head h at h*hd)
+hipError_t attention_forward(int dt, void* out, float* lse, const void* qkv, int B, int T, int H,
+                             int hd, hipStream_t s);
+// dqkv fully written.  scratch: attention_backward_scratch_bytes.
+size_t attention_backward_scratch_bytes(int B, int T, int H);
+hipError_t attention_backward(int dt, void* dqkv, const void* dout, const void* qkv,
+                              const void* out, const float* lse, int B, int T, int H, int hd,
+                              void* scratch, hipStream_t s);
+
+// ---- GEMM: C(m, n) = sum_k A(m, k) B(n, k), then an epilogue.
+// a_kmajor: A(m,k) = A[m*lda + k], else A[k*lda + m]; likewise b_kmajor for
+// B(n,k) = B[n*ldb + k] or B[k*ldb + n].  Leading dimensions are in
+// elements, multiples of 8, and each row must be readable up to
+// round_up(extent, 8).
+enum EpiMode {
+  EPI_STORE = 0,       // out = acc
+  EPI_BIAS = 1,        // out = acc + bias[n]
+  EPI_BIAS_RESID = 2,  // out = acc + bias[n] + resid[m, n]
+  EPI_BIAS_GELU = 3,   // out = acc + bias[n]; out2 = gelu(out)
+  EPI_GELU_BWD = 4,    // out = acc * gelu'(aux[m, n])
+  EPI_ACC_F32 = 5      // out (fp32) += acc
+};
+struct Epilogue {
+  int mode;
+  void* out;
+  int64_t ldo;
+  const float* bias;
+  const void* resid;
+  int64_t ldr;
+  void* out2;
+  int64_t ldo2;
+  const void* aux;
+  int64_t ldx;
+};
+hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
+                int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s);
+
+// ---- optimizer
+struct DecayMap {  // which flat elements belong to 2-D tensors
+  int64_t layer0, layer_size, n_layer_end;
+  int64_t qkvw0, qkvw1, projw0, projw1, fcw0, fcw1, fcpw0, fcpw1;  // offsets within a layer
+};
+size_t grad_norm_scratch_bytes();
+// writes norm (float) and clip scale min(1, clip/norm) to scratch; if
+// norm_out != nullptr also copies the norm there.
+hipError_t grad_norm(const float* g, int64_t n, float clip, void* scratch, float* norm_out,
+                     hipStream_t s);
+const float* grad_norm_result(const void* scratch);  // device pointer: [norm, scale]
+hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n,
+                 float lr, float b1, float b2, float eps, float wd, float bc1, float bc2,
+                 const float* norm_scale, DecayMap dm, hipStream_t s);
+hipError_t fill_f32(float* p, float value, int64_t n, hipStream_t s);
+hipError_t fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+hipError_t cast_f32_to_bf16(void* dst, const float* src, int64_t n, hipStream_t s);
+
+}  // namespace gk

@@ -1,0 +1,86 @@
+// Kernel-level C entry points (gpt2_kernels.h): argument checks, then the
+// same launchers the model runtime uses.
+#include <cstdio>
+#include <string>
+
+#include "../../include/gpt2.h"
+#include "../../include/gpt2_kernels.h"
+#include "kernels.h"
+
+extern "C" const char* gpt2_last_error(void);
+// defined in model.cpp
+int gpt2_internal_fail(int code, const char* msg);
+
+using namespace gk;
+
+static int launch_rc(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GPT2_OK;
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return gpt2_internal_fail(GPT2_EHIP, m.c_str());
+}
+
+extern "C" {
+
+int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const void* A,
+               int64_t lda, const void* B, int64_t ldb, int epilogue, void* out, int64_t ldo,
+               const float* bias, const void* resid, int64_t ldr, void* out2, int64_t ldo2,
+               const void* aux, int64_t ldx, void* stream) {
+  if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
+    return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
+  if (M < 0 || N < 0 || K < 0 || !A || !B || !out)
+    return gpt2_internal_fail(GPT2_EINVAL, "bad sizes or NULL operand");
+  if (epilogue < EPI_STORE || epilogue > EPI_ACC_F32)
+    return gpt2_internal_fail(GPT2_EINVAL, "unknown epilogue");
+  if (lda % 8 || ldb % 8) return gpt2_internal_fail(GPT2_EINVAL, "lda, ldb must be multiples of 8");
+  if ((epilogue == EPI_BIAS || epilogue == EPI_BIAS_RESID || epilogue == EPI_BIAS_GELU) && !bias)
+    return gpt2_internal_fail(GPT2_EINVAL, "epilogue needs bias");
+  if (epilogue == EPI_BIAS_RESID && !resid) return gpt2_internal_fail(GPT2_EINVAL, "needs resid");
+  if (epilogue == EPI_BIAS_GELU && !out2) return gpt2_internal_fail(GPT2_EINVAL, "needs out2");
+  if (epilogue == EPI_GELU_BWD && !aux) return gpt2_internal_fail(GPT2_EINVAL, "needs aux");
+  Epilogue e{};
+  e.mode = epilogue;
+  e.out = out;
+  e.ldo = ldo;
+  e.bias = bias;
+  e.resid = resid;
+  e.ldr = ldr;
+  e.out2 = out2;
+  e.ldo2 = ldo2;
+  e.aux = aux;
+  e.ldx = ldx;
+  return launch_rc(gemm(dtype, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb, e,
+                        (hipStream_t)stream),
+                   "gemm");
+}
+
+int gpt2k_attention_forward(int dtype, void* out, float* lse, const void* qkv, int B, int T, int H,
+                            int hd, void* stream) {
+  if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
+    return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
+  if (!out || !lse || !qkv || B < 1 || T < 1 || H < 1)
+    return gpt2_internal_fail(GPT2_EINVAL, "bad argument");
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return gpt2_internal_fail(GPT2_EINVAL, "head size must be 16, 32, 64 or 128");
+  return launch_rc(attention_forward(dtype, out, lse, qkv, B, T, H, hd, (hipStream_t)stream),
+                   "attention_forward");
+}
+
+size_t gpt2k_attention_backward_scratch_bytes(int B, int T, int H) {
+  return attention_backward_scratch_bytes(B, T, H);
+}
+
+int gpt2k_attention_backward(int dtype, void* dqkv, const void* dout, const void* qkv,
+                             const void* out, const float* lse, int B, int T, int H, int hd,
+                             void* scratch, void* stream) {
+  if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
+    return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
+  if (!dqkv || !dout || !qkv || !out || !lse || !scratch || B < 1 || T < 1 || H < 1)
+    return gpt2_internal_fail(GPT2_EINVAL, "bad argument");
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return gpt2_internal_fail(GPT2_EINVAL, "head size must be 16, 32, 64 or 128");
+  return launch_rc(attention_backward(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, scratch,
+                                      (hipStream_t)stream),
+                   "attention_backward");
+}
+
+}  // extern "C"

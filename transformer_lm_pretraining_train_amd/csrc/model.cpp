@@ -1,0 +1,621 @@
+// Runtime of libgpt2.so: config validation, the flat parameter layout, the
+// carve-up of the caller's single workspace, and the launch sequences of
+// forward, backward and the optimizer step on one HIP stream.
+//
+// The whole model state lives in the one workspace the caller allocates, in
+// this order (each region 256-byte aligned): fp32 parameters, gradients,
+// AdamW m and v; the bf16 copy of the parameters (bf16 mode); activations
+// kept for the backward; backward buffers; reduction scratch; flags.  The
+// library allocates nothing on the device after gpt2_create.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace gk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(GPT2_EHIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), __FILE__, \
+                  __LINE__);                                                              \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+
+struct TensorInfo {
+  std::string name;
+  int64_t offset;
+  int64_t rows, cols;  // cols == 1 for 1-D
+  int ndim;
+};
+
+struct LayerOffsets {
+  int64_t ln1_w, ln1_b, qkv_w, qkv_b, proj_w, proj_b, ln2_w, ln2_b, fc_w, fc_b, fcp_w, fcp_b;
+};
+
+struct Layout {
+  int64_t wte, wpe, lnf_w, lnf_b, total, layer0, layer_size;
+  std::vector<LayerOffsets> layers;
+  std::vector<TensorInfo> tensors;
+};
+
+// Flat order: wte, wpe, per layer (ln1 w/b, qkv w/b, proj w/b, ln2 w/b,
+// fc w/b, fcp w/b), lnf w/b.
+Layout make_layout(const gpt2_config& c) {
+  Layout L;
+  const int64_t C = c.n_embd;
+  int64_t off = 0;
+  auto add = [&](const std::string& name, int64_t rows, int64_t cols, int ndim) {
+    L.tensors.push_back({name, off, rows, cols, ndim});
+    int64_t o = off;
+    off += rows * cols;
+    return o;
+  };
+  L.wte = add("wte", c.padded_vocab_size, C, 2);
+  L.wpe = add("wpe", c.block_size, C, 2);
+  L.layer0 = off;
+  for (int l = 0; l < c.n_layer; ++l) {
+    std::string p = "h" + std::to_string(l) + ".";
+    LayerOffsets o;
+    o.ln1_w = add(p + "ln1_w", C, 1, 1);
+    o.ln1_b = add(p + "ln1_b", C, 1, 1);
+    o.qkv_w = add(p + "qkv_w", 3 * C, C, 2);
+    o.qkv_b = add(p + "qkv_b", 3 * C, 1, 1);
+    o.proj_w = add(p + "proj_w", C, C, 2);
+    o.proj_b = add(p + "proj_b", C, 1, 1);
+    o.ln2_w = add(p + "ln2_w", C, 1, 1);
+    o.ln2_b = add(p + "ln2_b", C, 1, 1);
+    o.fc_w = add(p + "fc_w", 4 * C, C, 2);
+    o.fc_b = add(p + "fc_b", 4 * C, 1, 1);
+    o.fcp_w = add(p + "fcp_w", C, 4 * C, 2);
+    o.fcp_b = add(p + "fcp_b", C, 1, 1);
+    L.layers.push_back(o);
+  }
+  L.layer_size = 12 * C * C + 13 * C;
+  L.lnf_w = add("lnf_w", C, 1, 1);
+  L.lnf_b = add("lnf_b", C, 1, 1);
+  L.total = off;
+  return L;
+}
+
+int validate(const gpt2_config* c) {
+  if (!c) return fail(GPT2_EINVAL, "config is NULL");
+  if (c->n_layer < 1 || c->n_head < 1) return fail(GPT2_EINVAL, "n_layer and n_head must be >= 1");
+  if (c->n_embd < 64 || c->n_embd % 64 != 0 || c->n_embd > 2048)
+    return fail(GPT2_EINVAL, "n_embd must be a multiple of 64 in [64, 2048], got %d", c->n_embd);
+  if (c->n_embd % c->n_head != 0) return fail(GPT2_EINVAL, "n_embd must be divisible by n_head");
+  int hd = c->n_embd / c->n_head;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return fail(GPT2_EINVAL, "head size %d not supported (16, 32, 64, 128)", hd);
+  if (c->seq_len < 1 || c->seq_len > c->block_size)
+    return fail(GPT2_EINVAL, "need 1 <= seq_len <= block_size");
+  if (c->vocab_size < 1 || c->padded_vocab_size < c->vocab_size)
+    return fail(GPT2_EINVAL, "need 1 <= vocab_size <= padded_vocab_size");
+  if (c->micro_batch < 1 || c->grad_accum_steps < 1)
+    return fail(GPT2_EINVAL, "micro_batch and grad_accum_steps must be >= 1");
+  if ((int64_t)c->micro_batch * c->seq_len > (1 << 24))
+    return fail(GPT2_EINVAL, "micro_batch * seq_len too large");
+  if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16) return fail(GPT2_EINVAL, "dtype must be 0 or 1");
+  if (c->deterministic)
+    return fail(GPT2_EINVAL,
+                "deterministic mode is not available: the embedding backward uses fp32 atomics");
+  if (!(c->ln_eps > 0.f)) return fail(GPT2_EINVAL, "ln_eps must be > 0");
+  return GPT2_OK;
+}
+
+}  // namespace
+
+int gpt2_internal_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+
+struct LayerAct {
+  void *ln1, *qkv, *atty, *res2, *ln2, *fch, *fchg, *res3;
+  float *ln1_mean, *ln1_rstd, *ln2_mean, *ln2_rstd, *lse;
+};
+
+struct gpt2_model {
+  gpt2_config cfg;
+  Layout lay;
+  hipStream_t stream;
+  int dt;
+  int L, H, C, hd, V, Vp, B, Tn, k;
+  int64_t M, N, ldl;
+  // state
+  float *params, *grads, *m, *v;
+  void* shadow;  // bf16 parameters (bf16 mode) or nullptr
+  // activations
+  void* encoded;
+  std::vector<LayerAct> act;
+  void* lnf;
+  float *lnf_mean, *lnf_rstd;
+  void* logits;
+  float *losses, *ce_lse, *loss_internal;
+  int32_t* argmax;
+  // backward
+  void *dres, *dbuf_c, *dbuf_4c, *dqkv;
+  void* scratch;
+  void* norm_scratch;
+  int* err_flag;
+  // bookkeeping
+  const int32_t* tokens;
+  const int32_t* targets;
+  bool have_targets;
+  int64_t step;
+
+  // weights in the GEMM input type
+  const void* wt(int64_t off) const {
+    return dt == BF16 ? (const void*)((const uint16_t*)shadow + off) : (const void*)(params + off);
+  }
+};
+
+namespace {
+
+// Walks the workspace plan; with base == nullptr it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  void* take(size_t bytes) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
+  Layout lay = make_layout(c);
+  Carver cv{base};
+  const int64_t C = c.n_embd, M = (int64_t)c.micro_batch * c.seq_len, N = lay.total;
+  const int dt = c.dtype;
+  const size_t es = dsize(dt);
+  const int64_t ldl = round_up(c.padded_vocab_size, 64);
+  const int H = c.n_head;
+  gpt2_model tmp;
+  gpt2_model& md = mdl ? *mdl : tmp;
+  md.params = (float*)cv.take(N * 4);
+  md.grads = (float*)cv.take(N * 4);
+  md.m = (float*)cv.take(N * 4);
+  md.v = (float*)cv.take(N * 4);
+  md.shadow = dt == BF16 ? cv.take(N * 2) : nullptr;
+  md.encoded = cv.take(M * C * es);
+  md.act.resize(c.n_layer);
+  for (int l = 0; l < c.n_layer; ++l) {
+    LayerAct& a = md.act[l];
+    a.ln1 = cv.take(M * C * es);
+    a.ln1_mean = (float*)cv.take(M * 4);
+    a.ln1_rstd = (float*)cv.take(M * 4);
+    a.qkv = cv.take(M * 3 * C * es);
+    a.atty = cv.take(M * C * es);
+    a.lse = (float*)cv.take((int64_t)c.micro_batch * H * c.seq_len * 4);
+    a.res2 = cv.take(M * C * es);
+    a.ln2 = cv.take(M * C * es);
+    a.ln2_mean = (float*)cv.take(M * 4);
+    a.ln2_rstd = (float*)cv.take(M * 4);
+    a.fch = cv.take(M * 4 * C * es);
+    a.fchg = cv.take(M * 4 * C * es);
+    a.res3 = cv.take(M * C * es);
+  }
+  md.lnf = cv.take(M * C * es);
+  md.lnf_mean = (float*)cv.take(M * 4);
+  md.lnf_rstd = (float*)cv.take(M * 4);
+  md.logits = cv.take(M * ldl * es);
+  md.losses = (float*)cv.take(M * 4);
+  md.ce_lse = (float*)cv.take(M * 4);
+  md.argmax = (int32_t*)cv.take(M * 4);
+  md.loss_internal = (float*)cv.take(4);
+  md.dres = cv.take(M * C * es);
+  md.dbuf_c = cv.take(M * C * es);
+  md.dbuf_4c = cv.take(M * 4 * C * es);
+  md.dqkv = cv.take(M * 3 * C * es);
+  size_t sc = layernorm_backward_scratch_bytes((int)M, (int)C);
+  sc = std::max(sc, bias_grad_scratch_bytes((int)M, (int)(4 * C)));
+  sc = std::max(sc, attention_backward_scratch_bytes(c.micro_batch, c.seq_len, H));
+  md.scratch = cv.take(sc);
+  md.norm_scratch = cv.take(grad_norm_scratch_bytes());
+  md.err_flag = (int*)cv.take(4);
+  return (cv.off + kAlign - 1) / kAlign * kAlign;
+}
+
+int check_launch(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GPT2_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return GPT2_OK;
+}
+
+#define LAUNCH(expr)                                 \
+  do {                                               \
+    int rc_ = check_launch((expr), #expr);           \
+    if (rc_ != GPT2_OK) return rc_;                  \
+  } while (0)
+
+Epilogue epi(int mode, void* out, int64_t ldo) {
+  Epilogue e{};
+  e.mode = mode;
+  e.out = out;
+  e.ldo = ldo;
+  return e;
+}
+
+DecayMap decay_map(const gpt2_model* md) {
+  const Layout& L = md->lay;
+  DecayMap d{};
+  d.layer0 = L.layer0;
+  d.layer_size = L.layer_size;
+  d.n_layer_end = L.layer0 + L.layer_size * md->L;
+  if (md->L > 0) {
+    const LayerOffsets& o = L.layers[0];
+    d.qkvw0 = o.qkv_w - L.layer0;
+    d.qkvw1 = d.qkvw0 + 3LL * md->C * md->C;
+    d.projw0 = o.proj_w - L.layer0;
+    d.projw1 = d.projw0 + (int64_t)md->C * md->C;
+    d.fcw0 = o.fc_w - L.layer0;
+    d.fcw1 = d.fcw0 + 4LL * md->C * md->C;
+    d.fcpw0 = o.fcp_w - L.layer0;
+    d.fcpw1 = d.fcpw0 + 4LL * md->C * md->C;
+  }
+  return d;
+}
+
+char* act_ptr(void* p, int64_t elems_offset, int dt) {
+  return (char*)p + elems_offset * dsize(dt);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt2_last_error(void) { return g_err.c_str(); }
+
+int64_t gpt2_num_params(const gpt2_config* cfg) {
+  if (!cfg) return -1;
+  gpt2_config c = *cfg;
+  c.deterministic = 0;
+  if (validate(&c) != GPT2_OK) return -1;
+  return make_layout(c).total;
+}
+
+size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
+  if (validate(cfg) != GPT2_OK) return 0;
+  return plan(*cfg, nullptr, nullptr);
+}
+
+int gpt2_param_layout(const gpt2_config* cfg, gpt2_tensor_info* out, int cap) {
+  if (!cfg) return fail(GPT2_EINVAL, "config is NULL");
+  gpt2_config c = *cfg;
+  c.deterministic = 0;
+  int rc = validate(&c);
+  if (rc != GPT2_OK) return rc;
+  Layout L = make_layout(c);
+  int n = (int)L.tensors.size();
+  if (out) {
+    for (int i = 0; i < n && i < cap; ++i) {
+      const TensorInfo& t = L.tensors[i];
+      memset(&out[i], 0, sizeof(out[i]));
+      snprintf(out[i].name, sizeof(out[i].name), "%s", t.name.c_str());
+      out[i].offset = t.offset;
+      out[i].ndim = t.ndim;
+      out[i].decay = t.ndim == 2 ? 1 : 0;
+      out[i].shape[0] = t.rows;
+      out[i].shape[1] = t.cols;
+    }
+  }
+  return n;
+}
+
+int gpt2_create(const gpt2_config* cfg, void* dev_workspace, size_t bytes, void* hip_stream,
+                gpt2_model** out) {
+  int rc = validate(cfg);
+  if (rc != GPT2_OK) return rc;
+  if (!out) return fail(GPT2_EINVAL, "out is NULL");
+  *out = nullptr;
+  size_t need = plan(*cfg, nullptr, nullptr);
+  if (!dev_workspace || bytes < need)
+    return fail(GPT2_EWORKSPACE, "workspace of %zu bytes, need %zu", bytes, need);
+  if ((uintptr_t)dev_workspace % kAlign != 0)
+    return fail(GPT2_EWORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  gpt2_model* md = new gpt2_model();
+  md->cfg = *cfg;
+  md->lay = make_layout(*cfg);
+  md->stream = (hipStream_t)hip_stream;
+  md->dt = cfg->dtype;
+  md->L = cfg->n_layer;
+  md->H = cfg->n_head;
+  md->C = cfg->n_embd;
+  md->hd = cfg->n_embd / cfg->n_head;
+  md->V = cfg->vocab_size;
+  md->Vp = cfg->padded_vocab_size;
+  md->B = cfg->micro_batch;
+  md->Tn = cfg->seq_len;
+  md->k = cfg->grad_accum_steps;
+  md->M = (int64_t)md->B * md->Tn;
+  md->N = md->lay.total;
+  md->ldl = round_up(md->Vp, 64);
+  plan(*cfg, (char*)dev_workspace, md);
+  md->tokens = md->targets = nullptr;
+  md->have_targets = false;
+  md->step = 0;
+  hipStream_t s = md->stream;
+  // zero all state (parameters, grads, m, v, shadow, logits padding, flags)
+  hipError_t e = fill_f32((float*)dev_workspace, 0.f, (int64_t)(need / 4), s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete md;
+    return fail(GPT2_EHIP, "initialising the workspace: %s", hipGetErrorString(e));
+  }
+  *out = md;
+  g_err.clear();
+  return GPT2_OK;
+}
+
+int gpt2_destroy(gpt2_model* md) {
+  delete md;
+  return GPT2_OK;
+}
+
+int gpt2_set_params(gpt2_model* md, const float* src) {
+  if (!md || !src) return fail(GPT2_EINVAL, "NULL argument");
+  HIP_TRY(hipMemcpyAsync(md->params, src, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  if (md->dt == BF16) LAUNCH(cast_f32_to_bf16(md->shadow, md->params, md->N, md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_get_params(gpt2_model* md, float* dst) {
+  if (!md || !dst) return fail(GPT2_EINVAL, "NULL argument");
+  HIP_TRY(hipMemcpyAsync(dst, md->params, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_get_grads(gpt2_model* md, float* dst) {
+  if (!md || !dst) return fail(GPT2_EINVAL, "NULL argument");
+  HIP_TRY(hipMemcpyAsync(dst, md->grads, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_set_grads(gpt2_model* md, const float* src) {
+  if (!md || !src) return fail(GPT2_EINVAL, "NULL argument");
+  HIP_TRY(hipMemcpyAsync(md->grads, src, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_get_opt_state(gpt2_model* md, float* dm, float* dv, int64_t* step) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (dm) HIP_TRY(hipMemcpyAsync(dm, md->m, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  if (dv) HIP_TRY(hipMemcpyAsync(dv, md->v, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  if (step) *step = md->step;
+  return GPT2_OK;
+}
+
+int gpt2_set_opt_state(gpt2_model* md, const float* dm, const float* dv, int64_t step) {
+  if (!md || !dm || !dv || step < 0) return fail(GPT2_EINVAL, "bad argument");
+  HIP_TRY(hipMemcpyAsync(md->m, dm, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  HIP_TRY(hipMemcpyAsync(md->v, dv, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
+  md->step = step;
+  return GPT2_OK;
+}
+
+int gpt2_zero_grad(gpt2_model* md) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  LAUNCH(fill_f32(md->grads, 0.f, md->N, md->stream));
+  return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, float* dev_loss) {
+  if (!md || !tokens) return fail(GPT2_EINVAL, "NULL argument");
+  const int dt = md->dt;
+  const int C = md->C, H = md->H, M = (int)md->M;
+  const Layout& Ly = md->lay;
+  hipStream_t s = md->stream;
+  const float eps = md->cfg.ln_eps;
+  float* P = md->params;
+  md->tokens = tokens;
+  md->targets = targets;
+  md->have_targets = false;
+
+  LAUNCH(encoder_forward(dt, md->encoded, tokens, P + Ly.wte, P + Ly.wpe, M, md->Tn, C, md->V,
+                         md->err_flag, s));
+  const void* x = md->encoded;
+  for (int l = 0; l < md->L; ++l) {
+    const LayerOffsets& o = Ly.layers[l];
+    LayerAct& a = md->act[l];
+    LAUNCH(layernorm_forward(dt, a.ln1, a.ln1_mean, a.ln1_rstd, x, P + o.ln1_w, P + o.ln1_b, M, C,
+                             eps, s));
+    Epilogue e = epi(EPI_BIAS, a.qkv, 3 * C);
+    e.bias = P + o.qkv_b;
+    LAUNCH(gemm(dt, true, true, M, 3 * C, C, a.ln1, C, md->wt(o.qkv_w), C, e, s));
+    LAUNCH(attention_forward(dt, a.atty, a.lse, a.qkv, md->B, md->Tn, H, md->hd, s));
+    e = epi(EPI_BIAS_RESID, a.res2, C);
+    e.bias = P + o.proj_b;
+    e.resid = x;
+    e.ldr = C;
+    LAUNCH(gemm(dt, true, true, M, C, C, a.atty, C, md->wt(o.proj_w), C, e, s));
+    LAUNCH(layernorm_forward(dt, a.ln2, a.ln2_mean, a.ln2_rstd, a.res2, P + o.ln2_w, P + o.ln2_b, M,
+                             C, eps, s));
+    e = epi(EPI_BIAS_GELU, a.fch, 4 * C);
+    e.bias = P + o.fc_b;
+    e.out2 = a.fchg;
+    e.ldo2 = 4 * C;
+    LAUNCH(gemm(dt, true, true, M, 4 * C, C, a.ln2, C, md->wt(o.fc_w), C, e, s));
+    e = epi(EPI_BIAS_RESID, a.res3, C);
+    e.bias = P + o.fcp_b;
+    e.resid = a.res2;
+    e.ldr = C;
+    LAUNCH(gemm(dt, true, true, M, C, 4 * C, a.fchg, 4 * C, md->wt(o.fcp_w), 4 * C, e, s));
+    x = a.res3;
+  }
+  LAUNCH(layernorm_forward(dt, md->lnf, md->lnf_mean, md->lnf_rstd, x, P + Ly.lnf_w, P + Ly.lnf_b,
+                           M, C, eps, s));
+  // logits over the padded vocabulary (tied head: wte)
+  LAUNCH(gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
+              epi(EPI_STORE, md->logits, md->ldl), s));
+  if (targets) {
+    LAUNCH(crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax, md->logits, md->ldl,
+                                targets, M, md->V, md->err_flag, s));
+    LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
+    md->have_targets = true;
+  }
+  return GPT2_OK;
+}
+
+int gpt2_backward(gpt2_model* md) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (!md->have_targets)
+    return fail(GPT2_ESTATE, "backward needs a preceding forward with targets");
+  md->have_targets = false;  // logits are overwritten below
+  const int dt = md->dt;
+  const int C = md->C, H = md->H, M = (int)md->M;
+  const Layout& Ly = md->lay;
+  hipStream_t s = md->stream;
+  float* P = md->params;
+  float* G = md->grads;
+  const float seed = (float)(1.0 / ((double)md->M * md->k));
+
+  // d logits, in place (columns >= V become 0)
+  LAUNCH(crossentropy_backward(dt, md->logits, md->ldl, md->ce_lse, md->targets, M, md->V, seed, s));
+  // tied head: dwte += dz^T lnf ; dlnf = dz wte
+  LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->logits, md->ldl, md->lnf, C,
+              epi(EPI_ACC_F32, G + Ly.wte, C), s));
+  LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->logits, md->ldl, md->wt(Ly.wte), C,
+              epi(EPI_STORE, md->dbuf_c, C), s));
+  const void* xfinal = md->L > 0 ? md->act[md->L - 1].res3 : md->encoded;
+  LAUNCH(fill_f32((float*)md->dres, 0.f, md->M * C * (int64_t)dsize(dt) / 4, s));
+  LAUNCH(layernorm_backward(dt, md->dres, G + Ly.lnf_w, G + Ly.lnf_b, md->dbuf_c, xfinal,
+                            md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C, md->scratch, s));
+  for (int l = md->L - 1; l >= 0; --l) {
+    const LayerOffsets& o = Ly.layers[l];
+    LayerAct& a = md->act[l];
+    const void* xin = l > 0 ? md->act[l - 1].res3 : md->encoded;
+    // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
+    LAUNCH(gemm(dt, false, false, C, 4 * C, M, md->dres, C, a.fchg, 4 * C,
+                epi(EPI_ACC_F32, G + o.fcp_w, 4 * C), s));
+    LAUNCH(bias_grad(dt, G + o.fcp_b, md->dres, M, C, C, md->scratch, s));
+    Epilogue e = epi(EPI_GELU_BWD, md->dbuf_4c, 4 * C);
+    e.aux = a.fch;
+    e.ldx = 4 * C;
+    LAUNCH(gemm(dt, true, false, M, 4 * C, C, md->dres, C, md->wt(o.fcp_w), 4 * C, e, s));
+    // fc: fch = ln2 fc_w^T + fc_b  (dbuf_4c now holds d fch)
+    LAUNCH(gemm(dt, false, false, 4 * C, C, M, md->dbuf_4c, 4 * C, a.ln2, C,
+                epi(EPI_ACC_F32, G + o.fc_w, C), s));
+    LAUNCH(bias_grad(dt, G + o.fc_b, md->dbuf_4c, M, 4 * C, 4 * C, md->scratch, s));
+    LAUNCH(gemm(dt, true, false, M, C, 4 * C, md->dbuf_4c, 4 * C, md->wt(o.fc_w), C,
+                epi(EPI_STORE, md->dbuf_c, C), s));
+    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln2_w, G + o.ln2_b, md->dbuf_c, a.res2,
+                              a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C, md->scratch, s));
+    // attention output projection: res2 = x + atty proj_w^T + proj_b
+    LAUNCH(gemm(dt, false, false, C, C, M, md->dres, C, a.atty, C,
+                epi(EPI_ACC_F32, G + o.proj_w, C), s));
+    LAUNCH(bias_grad(dt, G + o.proj_b, md->dres, M, C, C, md->scratch, s));
+    LAUNCH(gemm(dt, true, false, M, C, C, md->dres, C, md->wt(o.proj_w), C,
+                epi(EPI_STORE, md->dbuf_c, C), s));
+    LAUNCH(attention_backward(dt, md->dqkv, md->dbuf_c, a.qkv, a.atty, a.lse, md->B, md->Tn, H,
+                              md->hd, md->scratch, s));
+    // qkv = ln1 qkv_w^T + qkv_b
+    LAUNCH(gemm(dt, false, false, 3 * C, C, M, md->dqkv, 3 * C, a.ln1, C,
+                epi(EPI_ACC_F32, G + o.qkv_w, C), s));
+    LAUNCH(bias_grad(dt, G + o.qkv_b, md->dqkv, M, 3 * C, 3 * C, md->scratch, s));
+    LAUNCH(gemm(dt, true, false, M, C, 3 * C, md->dqkv, 3 * C, md->wt(o.qkv_w), C,
+                epi(EPI_STORE, md->dbuf_c, C), s));
+    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln1_w, G + o.ln1_b, md->dbuf_c, xin,
+                              a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, md->scratch, s));
+  }
+  // embeddings
+  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, s));
+  LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, md->dres, md->B, md->Tn, C, s));
+  return GPT2_OK;
+}
+
+int gpt2_sync(gpt2_model* md) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  HIP_TRY(hipStreamSynchronize(md->stream));
+  int flag = 0;
+  HIP_TRY(hipMemcpyAsync(&flag, md->err_flag, sizeof(int), hipMemcpyDeviceToHost, md->stream));
+  HIP_TRY(hipStreamSynchronize(md->stream));
+  if (flag) {
+    LAUNCH(fill_i32(md->err_flag, 0, 1, md->stream));
+    HIP_TRY(hipStreamSynchronize(md->stream));
+    return fail(GPT2_ETOKEN, "a token (bit 1) or target (bit 2) id was out of range: flags %d",
+                flag);
+  }
+  return GPT2_OK;
+}
+
+int gpt2_clip_and_adamw(gpt2_model* md, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, float grad_clip, float* dev_norm_out) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (!(grad_clip > 0.f)) return fail(GPT2_EINVAL, "grad_clip must be > 0");
+  hipStream_t s = md->stream;
+  LAUNCH(grad_norm(md->grads, md->N, grad_clip, md->norm_scratch, dev_norm_out, s));
+  const int64_t t = md->step + 1;
+  const float bc1 = (float)(1.0 - std::pow((double)beta1, (double)t));
+  const float bc2 = (float)(1.0 - std::pow((double)beta2, (double)t));
+  LAUNCH(adamw(md->params, md->grads, md->m, md->v, md->dt == BF16 ? md->shadow : nullptr, md->N,
+               lr, beta1, beta2, eps, weight_decay, bc1, bc2, grad_norm_result(md->norm_scratch),
+               decay_map(md), s));
+  float res[2] = {0.f, 0.f};
+  HIP_TRY(hipMemcpyAsync(res, grad_norm_result(md->norm_scratch), sizeof(res),
+                         hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (!std::isfinite(res[0]))
+    return fail(GPT2_ENONFINITE, "gradient norm is %f: update skipped", (double)res[0]);
+  md->step = t;
+  return gpt2_sync(md);
+}
+
+int gpt2_debug_read(gpt2_model* md, int which, int layer, void* dst, size_t bytes) {
+  if (!md || !dst) return fail(GPT2_EINVAL, "NULL argument");
+  const size_t es = dsize(md->dt);
+  const int64_t M = md->M, C = md->C;
+  const void* src = nullptr;
+  size_t n = 0;
+  auto need_layer = [&]() { return layer >= 0 && layer < md->L; };
+  switch (which) {
+    case GPT2_DBG_LOGITS: src = md->logits; n = M * md->ldl * es; break;
+    case GPT2_DBG_LOSSES: src = md->losses; n = M * 4; break;
+    case GPT2_DBG_ARGMAX: src = md->argmax; n = M * 4; break;
+    case GPT2_DBG_ACT_LNF: src = md->lnf; n = M * C * es; break;
+    case GPT2_DBG_ENCODED: src = md->encoded; n = M * C * es; break;
+    case GPT2_DBG_ACT_LN1:
+    case GPT2_DBG_ACT_QKV:
+    case GPT2_DBG_ACT_ATTY:
+    case GPT2_DBG_ACT_RES2:
+    case GPT2_DBG_ACT_FCH:
+    case GPT2_DBG_ACT_RES3:
+    case GPT2_DBG_ATT_LSE: {
+      if (!need_layer()) return fail(GPT2_EINVAL, "layer %d out of range", layer);
+      const LayerAct& a = md->act[layer];
+      if (which == GPT2_DBG_ACT_LN1) { src = a.ln1; n = M * C * es; }
+      if (which == GPT2_DBG_ACT_QKV) { src = a.qkv; n = M * 3 * C * es; }
+      if (which == GPT2_DBG_ACT_ATTY) { src = a.atty; n = M * C * es; }
+      if (which == GPT2_DBG_ACT_RES2) { src = a.res2; n = M * C * es; }
+      if (which == GPT2_DBG_ACT_FCH) { src = a.fch; n = M * 4 * C * es; }
+      if (which == GPT2_DBG_ACT_RES3) { src = a.res3; n = M * C * es; }
+      if (which == GPT2_DBG_ATT_LSE) { src = a.lse; n = (size_t)md->B * md->H * md->Tn * 4; }
+      break;
+    }
+    default: return fail(GPT2_EINVAL, "unknown debug buffer %d", which);
+  }
+  if (bytes < n) return fail(GPT2_EINVAL, "destination holds %zu bytes, need %zu", bytes, n);
+  HIP_TRY(hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, md->stream));
+  return GPT2_OK;
+}
+
+}  // extern "C"
