@@ -74,7 +74,7 @@ def roofline_lm_head(cfg, stream):
                                    stream=stream), stream)
     flops = 2.0 * M * N * K
     achieved = flops / t / 1e12
-    return {"kernel": "gemm_mfma_kernel<true,true,EPI_STORE> (lm_head forward, "
+    return {"kernel": "gemm_big_kernel<256,256,true,true,EPI_STORE> (lm_head forward, "
                       f"M={M} N={N} K={K})",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,

@@ -39,11 +39,16 @@ enum {
  * Leading dimensions (elements) must be multiples of 8, and each row of A
  * and B must be readable up to round_up(extent, 8) elements.  Output
  * leading dimensions ldo, ldr, ldo2, ldx are in elements.  Pointers not used
- * by the epilogue may be NULL. */
+ * by the epilogue may be NULL.  For GPT2K_EPI_ACC_F32 the K range may be
+ * split over several workgroups whose fp32 partial tiles are summed in a
+ * fixed order; that needs gpt2k_gemm_workspace_bytes() of scratch in dev_ws
+ * (with less, the product runs unsplit). */
+size_t gpt2k_gemm_workspace_bytes(int dtype, int M, int N, int K, int epilogue);
 int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const void* dev_A,
                int64_t lda, const void* dev_B, int64_t ldb, int epilogue, void* dev_out,
                int64_t ldo, const float* dev_bias, const void* dev_resid, int64_t ldr,
-               void* dev_out2, int64_t ldo2, const void* dev_aux, int64_t ldx, void* hip_stream);
+               void* dev_out2, int64_t ldo2, const void* dev_aux, int64_t ldx, void* dev_ws,
+               size_t ws_bytes, void* hip_stream);
 
 /* Causal self-attention forward on qkv (B*T, 3C) rows [q | k | v], head h at
  * columns h*hd within each third, C = H*hd: out (B*T, C) = softmax(q k^T /

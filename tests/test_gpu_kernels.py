@@ -132,6 +132,33 @@ def test_gemm_gpt2_124m_shapes_sampled(akm, bkm, M, N, K):
     ref = Am @ Bm.T
     got = out[ridx].float().cpu().numpy()
     assert rel_l2(got, ref) < 4e-3
+    if not akm:
+        # weight-gradient form: fp32 accumulation into an existing gradient
+        # (split over K when the output grid is small)
+        init = torch.randn((M, N), device="cuda", generator=gen)
+        acc = init.clone()
+        g.gemm(BF16, akm, bkm, M, N, K, A, A.shape[1], B, B.shape[1], "acc_f32", acc, N)
+        torch.cuda.synchronize()
+        ref2 = init[ridx].cpu().numpy().astype(np.float64) + ref
+        assert rel_l2(acc[ridx].cpu().numpy(), ref2) < 1e-5
+
+
+@pytest.mark.parametrize("M,N", [(768, 3072), (3072, 768), (768, 768), (2304, 768)])
+def test_gemm_weight_gradient_split_k(M, N):
+    """The four per-layer weight-gradient products at the 124M shapes
+    (K = B*T = 16384), fp32-accumulated, full output against fp64."""
+    K = 16384
+    print(f"gemm dW M={M} N={N} K={K} ws={g.gemm_workspace_bytes(BF16, M, N, K, 'acc_f32')}",
+          flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(M + N)
+    A = torch.randn((K, M), device="cuda", generator=gen).to(torch.bfloat16)
+    B = torch.randn((K, N), device="cuda", generator=gen).to(torch.bfloat16)
+    init = torch.randn((M, N), device="cuda", generator=gen)
+    out = init.clone()
+    g.gemm(BF16, False, False, M, N, K, A, M, B, N, "acc_f32", out, N)
+    ref = init.double() + A.double().T @ B.double()
+    torch.cuda.synchronize()
+    assert rel_l2(out.cpu().numpy(), ref.cpu().numpy()) < 1e-5
 
 
 # ------------------------------------------------------------------ attention

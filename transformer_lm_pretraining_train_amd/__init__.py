@@ -15,7 +15,7 @@ import os
 
 __all__ = [
     "GPT2Config", "TensorInfo", "GPT2Error", "lib", "library_path", "Model", "param_layout",
-    "num_params", "workspace_bytes", "gemm", "attention_forward", "attention_backward",
+    "num_params", "workspace_bytes", "gemm", "gemm_workspace_bytes", "attention_forward", "attention_backward",
     "attention_backward_scratch_bytes", "flops_per_token", "config_for",
     "GPT2_FP32", "GPT2_BF16", "EPI",
 ]
@@ -87,7 +87,8 @@ def lib() -> ctypes.CDLL:
             "gpt2_debug_read": (I, [P, I, I, P, SZ]),
             "gpt2_last_error": (ctypes.c_char_p, []),
             "gpt2k_gemm": (I, [I, I, I, I, I, I, P, I64, P, I64, I, P, I64, P, P, I64, P, I64, P,
-                               I64, P]),
+                               I64, P, SZ, P]),
+            "gpt2k_gemm_workspace_bytes": (SZ, [I, I, I, I, I]),
             "gpt2k_attention_forward": (I, [I, P, P, P, I, I, I, I, P]),
             "gpt2k_attention_backward_scratch_bytes": (SZ, [I, I, I]),
             "gpt2k_attention_backward": (I, [I, P, P, P, P, P, I, I, I, I, P, P]),
@@ -249,12 +250,26 @@ class Model:
 
 
 # ---- kernel-level entry points
+def gemm_workspace_bytes(dtype, M, N, K, epilogue):
+    epi = EPI[epilogue] if isinstance(epilogue, str) else epilogue
+    return lib().gpt2k_gemm_workspace_bytes(dtype, M, N, K, epi)
+
+
 def gemm(dtype, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, epilogue, out, ldo, bias=None,
-         resid=None, ldr=0, out2=None, ldo2=0, aux=None, ldx=0, stream=None):
+         resid=None, ldr=0, out2=None, ldo2=0, aux=None, ldx=0, ws=None, stream=None):
+    """C(m, n) = sum_k A(m, k) B(n, k) + epilogue (see gpt2_kernels.h).  For the
+    fp32-accumulating epilogue a split-K workspace is allocated here when
+    ``ws`` is None and the product would use one."""
+    epi = EPI[epilogue] if isinstance(epilogue, str) else epilogue
+    if ws is None:
+        nb = gemm_workspace_bytes(dtype, M, N, K, epi)
+        if nb:
+            import torch
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gpt2k_gemm(dtype, int(a_kmajor), int(b_kmajor), M, N, K, _ptr(A), lda, _ptr(B),
-                            ldb, EPI[epilogue] if isinstance(epilogue, str) else epilogue,
-                            _ptr(out), ldo, _ptr(bias), _ptr(resid), ldr, _ptr(out2), ldo2,
-                            _ptr(aux), ldx, _stream(stream)))
+                            ldb, epi, _ptr(out), ldo, _ptr(bias), _ptr(resid), ldr, _ptr(out2),
+                            ldo2, _ptr(aux), ldx, _ptr(ws), nbytes, _stream(stream)))
 
 
 def attention_forward(dtype, out, lse, qkv, B, T, H, hd, stream=None):

@@ -1,17 +1,486 @@
-// Matrix-core (MFMA) flash attention for bf16, head size 64.
+// Matrix-core flash attention for bf16, head size 64, on gfx950
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation and softmax).
+//
+// Causal self-attention per (batch, head): S = q k^T / sqrt(64), j <= i,
+// P = softmax_j(S), O = P v; the forward also stores the log-sum-exp L of
+// each query row.  The T x T matrix is never stored: 64-key (or 64-query)
+// tiles are staged through LDS and the softmax is computed online.
+//
+// Register layout.  A wave owns 32 queries (forward, dQ) or 32 keys (dK/dV).
+// Scores are produced transposed where that keeps a lane on one query:
+// S^T = K Q^T gives each lane one query column and 16 key rows of a 32 x 32
+// tile (accumulator row = 8*(r/4) + 4*(lane/32) + r%4), so the row maximum
+// needs one exchange with lane^32 and the probabilities are already laid
+// out as the B operand of the next product O^T += V^T P^T: lane half h of
+// slot j holds key 4h + j (j < 4) or 8 + 4h + j - 4 (j >= 4) of each
+// 16-key step.
+//
+// LDS tiles are always stored as they sit in memory, [row][d] (16-byte
+// copies).  Operands that need the transposed tile (V^T, K^T, Q^T, dO^T)
+// are read with ds_read_b64_tr_b16: within each 16-lane group, lane j gets
+// element j%4 of the 8-byte rows addressed by lanes j/4 + 4e (e = 0..3), so
+// pointing lane i' at row kbase + i'/4, column c0 + 4 (i'%4) hands lane j
+// rows kbase .. kbase+3 of column c0 + j -- four k-values of one MFMA
+// operand row, in the permuted key order above.
+//
+// Backward (no atomics):
+//   dQ pass, per query block: D_i = dO_i . O_i (stored for the next pass),
+//     S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+//   dK/dV pass, per key block: S = Q K^T, dP = dO V^T (lane owns a key
+//     column), P = exp(S - L), dS = P (dP - D), dV^T += dO^T P,
+//     dK^T += Q^T dS.
+// LDS is double-buffered (one barrier per tile) with the next tile's global
+// loads in flight during the current tile's math.  Workgroups of the causal
+// passes are issued longest-first.
 #include "common.h"
 #include "kernels.h"
 
 namespace gk {
 
-bool attention_mfma_supported(int dt, int hd) { return false; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-hipError_t attention_forward_mfma(void*, float*, const void*, int, int, int, hipStream_t) {
-  return hipErrorInvalidValue;
+namespace {
+
+constexpr int HD = 64;    // head size
+constexpr int WQ = 128;   // queries (or keys) per workgroup: 4 waves x 32
+constexpr int TB = 64;    // keys (or queries) per LDS tile
+constexpr int PR = 72;    // LDS pitch of [row][d] tiles (elements; 144 B, 16 B aligned)
+constexpr int TILE = TB * PR;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-hipError_t attention_backward_mfma(void*, const void*, const void*, const void*, const float*,
-                                   float*, int, int, int, hipStream_t) {
-  return hipErrorInvalidValue;
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row of the accumulator held in register r by lane half h2.
+__device__ __forceinline__ int acc_row(int r, int h2) { return 8 * (r / 4) + 4 * h2 + (r % 4); }
+
+// 64 rows x 64 columns of bf16 from global (row stride ld), rows >= nrows
+// read as zero: two 16-byte chunks per thread.
+struct TileRegs {
+  uint4 v[2];
+};
+__device__ __forceinline__ void tile_load(TileRegs& R, const bf16* __restrict__ src, int64_t ld,
+                                          int row0, int nrows) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int c = threadIdx.x + 256 * i;
+    int row = c / 8, d = (c % 8) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row0 + row < nrows) v = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + row) * ld + d);
+    R.v[i] = v;
+  }
+}
+__device__ __forceinline__ void tile_store(const TileRegs& R, bf16* __restrict__ S) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int c = threadIdx.x + 256 * i;
+    int row = c / 8, d = (c % 8) * 8;
+    *reinterpret_cast<uint4*>(S + row * PR + d) = R.v[i];
+  }
+}
+
+// Fragment from a row-major tile: row `row`, k = ks*16 + h2*8 .. +8.
+__device__ __forceinline__ bf16x8_t frag_rows(const bf16* S, int row, int ks, int h2) {
+  return *reinterpret_cast<const bf16x8_t*>(S + row * PR + ks * 16 + h2 * 8);
+}
+
+__device__ __forceinline__ v4i16 ds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+}
+
+// Transposed fragment: lane l gets column c0 + l%32 of the tile at rows
+// kb + 4*h2 .. +4 and kb + 8 + 4*h2 .. +4 (the accumulator key order).
+__device__ __forceinline__ bf16x8_t frag_tr(const bf16* S, int c0, int kb, int lane) {
+  const int j = lane % 16, h2 = lane / 32;
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const v4i16 lo = ds_read_tr(S + (kb + 4 * h2 + (j >> 2)) * PR + col);
+  const v4i16 hi = ds_read_tr(S + (kb + 8 + 4 * h2 + (j >> 2)) * PR + col);
+  union {
+    v4i16 s[2];
+    bf16x8_t v;
+  } r;
+  r.s[0] = lo;
+  r.s[1] = hi;
+  return r.v;
+}
+
+// Registers 8u .. 8u+7 of an accumulator as a bf16 B operand.
+__device__ __forceinline__ bf16x8_t pack_b(const f32x16_t& a, int u) {
+  bf16x8_t r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (bf16)a[8 * u + j];
+  return r;
+}
+// Global fragment of one row: 8 consecutive bf16 at d = ks*16 + h2*8.
+__device__ __forceinline__ bf16x8_t frag_global(const bf16* __restrict__ row_ptr, int ks, int h2,
+                                                bool valid) {
+  union {
+    uint4 u;
+    bf16x8_t v;
+  } r;
+  r.u = valid ? *reinterpret_cast<const uint4*>(row_ptr + ks * 16 + h2 * 8) : make_uint4(0, 0, 0, 0);
+  return r.v;
+}
+
+// Writes the 16 values of a transposed accumulator (lane: one row of the
+// output, d = dbase + acc_row(r)) as 4 groups of 4 consecutive bf16.
+__device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x16_t& a, float mul,
+                                              int dbase, int h2) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    int d = dbase + 8 * g + 4 * h2;
+    union {
+      uint2 u;
+      bf16 e[4];
+    } w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.e[j] = (bf16)(a[4 * g + j] * mul);
+    *reinterpret_cast<uint2*>(dst + d) = w.u;
+  }
+}
+
+// --------------------------------------------------------------- forward
+__global__ __launch_bounds__(256) void attn_fwd_mfma(bf16* __restrict__ out, float* __restrict__ lse,
+                                                     const bf16* __restrict__ qkv, int T, int H,
+                                                     int nqb) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int C = H * HD;
+  const int64_t ld = 3LL * C;
+  const bf16* base = qkv + (int64_t)b * T * ld;
+  const bf16* kbase = base + C + hh * HD;
+  const bf16* vbase = base + 2 * C + hh * HD;
+  const int q0 = qb * WQ, qw = q0 + wave * 32, myq = qw + l32;
+  const float c = 0.125f * LOG2E;  // 1/sqrt(64) in log2 units
+
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qf[ks] = frag_global(base + (int64_t)myq * ld + hh * HD, ks, h2, myq < T);
+  f32x16_t o[2] = {zero16(), zero16()};
+  float m = -INFINITY, l = 0.f;
+  const int nkb = (int)min(cdiv(q0 + WQ, TB), cdiv(T, TB));
+  TileRegs rk, rv;
+  tile_load(rk, kbase, ld, 0, T);
+  tile_load(rv, vbase, ld, 0, T);
+  tile_store(rk, smem);
+  tile_store(rv, smem + TILE);
+  if (nkb > 1) {
+    tile_load(rk, kbase, ld, TB, T);
+    tile_load(rv, vbase, ld, TB, T);
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    const bf16* Vs = Ks + TILE;
+    if (kb + 1 < nkb) {
+      bf16* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
+      tile_store(rk, nxt);
+      tile_store(rv, nxt + TILE);
+      if (kb + 2 < nkb) {
+        tile_load(rk, kbase, ld, (kb + 2) * TB, T);
+        tile_load(rv, vbase, ld, (kb + 2) * TB, T);
+      }
+    }
+    const int k0 = kb * TB;
+    if (k0 <= qw + 31 && qw < T) {
+      f32x16_t s[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s[t] = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s[t]);
+      const bool diag = k0 + TB - 1 > qw;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[t][r] * c;
+          if (diag && k0 + t * 32 + acc_row(r, h2) > myq) x = -INFINITY;
+          s[t][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m, mx);
+      const float alpha = exp2_(m - mnew);
+      m = mnew;
+      l *= alpha;
+      o[0] *= alpha;
+      o[1] *= alpha;
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_(s[t][r] - mnew);
+          s[t][r] = p;
+          ps += p;
+        }
+      l += ps;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t pb = pack_b(s[t], u);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+            o[dt] = mfma(frag_tr(Vs, dt * 32, t * 32 + 16 * u, lane), pb, o[dt]);
+        }
+    }
+    __syncthreads();
+  }
+  l += __shfl_xor(l, 32, 64);
+  if (myq < T) {
+    const float inv = 1.0f / l;
+    bf16* dst = out + ((int64_t)b * T + myq) * C + hh * HD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) store_acc_row(dst, o[dt], inv, dt * 32, h2);
+    if (h2 == 0) lse[(int64_t)bh * T + myq] = (m + __builtin_amdgcn_logf(l)) * LN2;
+  }
+}
+
+// --------------------------------------------------------------- backward: dQ
+__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
+                                                        const bf16* __restrict__ dout,
+                                                        const bf16* __restrict__ qkv,
+                                                        const bf16* __restrict__ out,
+                                                        const float* __restrict__ lse, int T, int H,
+                                                        int nqb) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
+  const int qb = nqb - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int C = H * HD;
+  const int64_t ld = 3LL * C;
+  const bf16* base = qkv + (int64_t)b * T * ld;
+  const bf16* kbase = base + C + hh * HD;
+  const bf16* vbase = base + 2 * C + hh * HD;
+  const int q0 = qb * WQ, qw = q0 + wave * 32, myq = qw + l32;
+  const bool qvalid = myq < T;
+  const float c = 0.125f * LOG2E;
+
+  bf16x8_t qf[4], df[4];
+  const bf16* dorow = dout + ((int64_t)b * T + myq) * C + hh * HD;
+  const bf16* orow = out + ((int64_t)b * T + myq) * C + hh * HD;
+  float Dp = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qf[ks] = frag_global(base + (int64_t)myq * ld + hh * HD, ks, h2, qvalid);
+    df[ks] = frag_global(dorow, ks, h2, qvalid);
+    bf16x8_t of = frag_global(orow, ks, h2, qvalid);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Dp += (float)df[ks][j] * (float)of[j];
+  }
+  const float Dq = Dp + __shfl_xor(Dp, 32, 64);
+  const float L2 = qvalid ? lse[(int64_t)bh * T + myq] * LOG2E : 0.f;
+  if (qvalid && h2 == 0) Dbuf[(int64_t)bh * T + myq] = Dq;
+
+  f32x16_t dq[2] = {zero16(), zero16()};
+  const int nkb = (int)min(cdiv(q0 + WQ, TB), cdiv(T, TB));
+  TileRegs rk, rv;
+  tile_load(rk, kbase, ld, 0, T);
+  tile_load(rv, vbase, ld, 0, T);
+  tile_store(rk, smem);
+  tile_store(rv, smem + TILE);
+  if (nkb > 1) {
+    tile_load(rk, kbase, ld, TB, T);
+    tile_load(rv, vbase, ld, TB, T);
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    const bf16* Vs = Ks + TILE;
+    if (kb + 1 < nkb) {
+      bf16* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
+      tile_store(rk, nxt);
+      tile_store(rv, nxt + TILE);
+      if (kb + 2 < nkb) {
+        tile_load(rk, kbase, ld, (kb + 2) * TB, T);
+        tile_load(rv, vbase, ld, (kb + 2) * TB, T);
+      }
+    }
+    const int k0 = kb * TB;
+    if (k0 <= qw + 31 && qw < T) {
+      const bool diag = k0 + TB - 1 > qw;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          s = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s);
+          dp = mfma(frag_rows(Vs, t * 32 + l32, ks, h2), df[ks], dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_(s[r] * c - L2);
+          if (diag && k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
+          s[r] = p * (dp[r] - Dq);  // dS^T
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t sb = pack_b(s, u);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+            dq[dt] = mfma(frag_tr(Ks, dt * 32, t * 32 + 16 * u, lane), sb, dq[dt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (qvalid) {
+    bf16* dst = dqkv + ((int64_t)b * T + myq) * ld + hh * HD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) store_acc_row(dst, dq[dt], 0.125f, dt * 32, h2);
+  }
+}
+
+// --------------------------------------------------------------- backward: dK, dV
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkv_mfma(bf16* __restrict__ dqkv,
+                                                         const float* __restrict__ Dbuf,
+                                                         const bf16* __restrict__ dout,
+                                                         const bf16* __restrict__ qkv,
+                                                         const float* __restrict__ lse, int T, int H) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][Q | dO]
+  __shared__ __attribute__((aligned(16))) float LD[2][2][TB];   // [stage][L | D]
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
+  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int C = H * HD;
+  const int64_t ld = 3LL * C;
+  const bf16* base = qkv + (int64_t)b * T * ld;
+  const bf16* qbase = base + hh * HD;
+  const bf16* dobase = dout + (int64_t)b * T * C + hh * HD;
+  const int k0w = blockIdx.x * WQ, kw = k0w + wave * 32, mykey = kw + l32;
+  const bool kvalid = mykey < T;
+  const float c = 0.125f * LOG2E;
+
+  bf16x8_t kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = frag_global(base + (int64_t)mykey * ld + C + hh * HD, ks, h2, kvalid);
+    vf[ks] = frag_global(base + (int64_t)mykey * ld + 2 * C + hh * HD, ks, h2, kvalid);
+  }
+  f32x16_t dk[2] = {zero16(), zero16()}, dv[2] = {zero16(), zero16()};
+  const int qb0 = k0w / TB, nqb = (int)cdiv(T, TB);
+  TileRegs rq, rd;
+  float lsv = 0.f, dsv = 0.f;
+  auto gload = [&](int qb) {
+    tile_load(rq, qbase, ld, qb * TB, T);
+    tile_load(rd, dobase, C, qb * TB, T);
+    if (threadIdx.x < TB) {
+      int q = qb * TB + threadIdx.x;
+      lsv = q < T ? lse[(int64_t)bh * T + q] * LOG2E : INFINITY;
+      dsv = q < T ? Dbuf[(int64_t)bh * T + q] : 0.f;
+    }
+  };
+  auto sstore = [&](int stage) {
+    bf16* dst = smem + stage * 2 * TILE;
+    tile_store(rq, dst);
+    tile_store(rd, dst + TILE);
+    if (threadIdx.x < TB) {
+      LD[stage][0][threadIdx.x] = lsv;
+      LD[stage][1][threadIdx.x] = dsv;
+    }
+  };
+  gload(qb0);
+  sstore(0);
+  if (qb0 + 1 < nqb) gload(qb0 + 1);
+  __syncthreads();
+  for (int qb = qb0; qb < nqb; ++qb) {
+    const int stage = (qb - qb0) & 1;
+    const bf16* Qs = smem + stage * 2 * TILE;
+    const bf16* Os = Qs + TILE;
+    const float* Ls = LD[stage][0];
+    const float* Ds = LD[stage][1];
+    if (qb + 1 < nqb) {
+      sstore(stage ^ 1);
+      if (qb + 2 < nqb) gload(qb + 2);
+    }
+    const int qs0 = qb * TB;
+    if (qs0 + TB - 1 >= kw && kw < T) {
+      const bool diag = qs0 < kw + 31;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          s = mfma(frag_rows(Qs, t * 32 + l32, ks, h2), kf[ks], s);
+          dp = mfma(frag_rows(Os, t * 32 + l32, ks, h2), vf[ks], dp);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int rowb = t * 32 + 8 * g + 4 * h2;  // query rows rowb .. rowb+3 of the tile
+          const float4 L4 = *reinterpret_cast<const float4*>(Ls + rowb);
+          const float4 D4 = *reinterpret_cast<const float4*>(Ds + rowb);
+          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * g + j;
+            float p = exp2_(s[r] * c - Lv[j]);
+            if (diag && qs0 + rowb + j < mykey) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - Dv[j]);  // dS
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t pb = pack_b(s, u);
+          bf16x8_t sb = pack_b(dp, u);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            dv[dt] = mfma(frag_tr(Os, dt * 32, t * 32 + 16 * u, lane), pb, dv[dt]);
+            dk[dt] = mfma(frag_tr(Qs, dt * 32, t * 32 + 16 * u, lane), sb, dk[dt]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (kvalid) {
+    bf16* dst = dqkv + ((int64_t)b * T + mykey) * ld + hh * HD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      store_acc_row(dst + C, dk[dt], 0.125f, dt * 32, h2);
+      store_acc_row(dst + 2 * C, dv[dt], 1.0f, dt * 32, h2);
+    }
+  }
+}
+
+}  // namespace
+
+bool attention_mfma_supported(int dt, int hd) { return dt == BF16 && hd == HD; }
+
+hipError_t attention_forward_mfma(void* out, float* lse, const void* qkv, int B, int T, int H,
+                                  hipStream_t s) {
+  const int nqb = (int)cdiv(T, WQ);
+  dim3 grid((unsigned)nqb, (unsigned)(B * H));
+  attn_fwd_mfma<<<grid, 256, 0, s>>>((bf16*)out, lse, (const bf16*)qkv, T, H, nqb);
+  return hipGetLastError();
+}
+
+hipError_t attention_backward_mfma(void* dqkv, const void* dout, const void* qkv, const void* out,
+                                   const float* lse, float* Dbuf, int B, int T, int H,
+                                   hipStream_t s) {
+  const int nb = (int)cdiv(T, WQ);
+  dim3 grid((unsigned)nb, (unsigned)(B * H));
+  attn_bwd_dq_mfma<<<grid, 256, 0, s>>>((bf16*)dqkv, Dbuf, (const bf16*)dout, (const bf16*)qkv,
+                                        (const bf16*)out, lse, T, H, nb);
+  attn_bwd_dkv_mfma<<<grid, 256, 0, s>>>((bf16*)dqkv, Dbuf, (const bf16*)dout, (const bf16*)qkv,
+                                         lse, T, H);
+  return hipGetLastError();
 }
 
 }  // namespace gk

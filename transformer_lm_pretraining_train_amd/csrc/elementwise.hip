@@ -293,19 +293,32 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) dst[c] = red[c];
 }
 
-// out[c] += sum_b partial[b][c] over nb blocks, c < n (fixed order).
-__global__ void column_partials_reduce_kernel(float* __restrict__ out0, float* __restrict__ out1,
-                                              const float* __restrict__ partial, int nb, int C,
-                                              int stride) {
-  int c = blockIdx.x * blockDim.x + threadIdx.x;
-  int total = out1 ? 2 * C : C;
-  if (c >= total) return;
+// out0[c] += sum_b partial[b * stride + c] for c < C, and out1[c - C] for
+// C <= c < 2C when out1 is given.  256 threads = 32 columns x 8 groups of
+// partials; each group sums every 8th partial, then the 8 group sums are
+// added in a fixed order.
+__global__ __launch_bounds__(256) void column_partials_reduce_kernel(float* __restrict__ out0,
+                                                                     float* __restrict__ out1,
+                                                                     const float* __restrict__ partial,
+                                                                     int nb, int C, int stride) {
+  __shared__ float red[8][33];
+  const int lc = threadIdx.x % 32, g = threadIdx.x / 32;
+  const int c = blockIdx.x * 32 + lc;
+  const int total = out1 ? 2 * C : C;
   float acc = 0.f;
-  for (int b = 0; b < nb; ++b) acc += partial[(int64_t)b * stride + c];
-  if (c < C)
-    out0[c] += acc;
-  else
-    out1[c - C] += acc;
+  if (c < total)
+    for (int b = g; b < nb; b += 8) acc += partial[(int64_t)b * stride + c];
+  red[g][lc] = acc;
+  __syncthreads();
+  if (g == 0 && c < total) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t += red[k][lc];
+    if (c < C)
+      out0[c] += t;
+    else
+      out1[c - C] += t;
+  }
 }
 
 size_t layernorm_backward_scratch_bytes(int M, int C) {
@@ -320,8 +333,8 @@ hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, const vo
   float* partial = (float*)scratch;
   DISPATCH_DT(dt, layernorm_bwd_kernel<T><<<nb, 256, 2 * C * sizeof(float), s>>>(
                       (T*)dres, partial, (const T*)dy, (const T*)inp, mean, rstd, w, M, C));
-  column_partials_reduce_kernel<<<grid_for(2 * C, 256), 256, 0, s>>>(dw, db, partial, nb, C,
-                                                                      2 * C);
+  column_partials_reduce_kernel<<<grid_for(2 * C, 32), 256, 0, s>>>(dw, db, partial, nb, C,
+                                                                     2 * C);
   return hipGetLastError();
 }
 
@@ -370,8 +383,8 @@ hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ld
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)cdiv(M, BG_ROWS));
   float* partial = (float*)scratch;
   DISPATCH_DT(dt, bias_grad_kernel<T><<<grid, 256, 0, s>>>(partial, (const T*)dy, M, N, ldy));
-  column_partials_reduce_kernel<<<grid_for(N, 256), 256, 0, s>>>(db, nullptr, partial,
-                                                                  (int)grid.y, N, N);
+  column_partials_reduce_kernel<<<grid_for(N, 32), 256, 0, s>>>(db, nullptr, partial,
+                                                                 (int)grid.y, N, N);
   return hipGetLastError();
 }
 
@@ -577,33 +590,57 @@ __device__ __forceinline__ bool decays(int64_t i, const DecayMap& d) {
          (r >= d.fcw0 && r < d.fcw1) || (r >= d.fcpw0 && r < d.fcpw1);
 }
 
+__device__ __forceinline__ void adamw_elem(float& p, float& m, float& v, float g, float b1, float b2,
+                                           float eps, float dec, float lr, float bc1, float bc2) {
+  m = b1 * m + (1.f - b1) * g;
+  v = b2 * v + (1.f - b2) * g * g;
+  const float mhat = m / bc1;
+  const float vhat = v / bc2;
+  p -= lr * (mhat / (sqrtf(vhat) + eps) + dec * p);
+}
+
 // One thread per 4 elements (tensor boundaries are multiples of C, C % 64 == 0,
-// so a group of 4 never straddles two tensors).  Skips everything when the
-// norm is not finite.
+// so a group of 4 never straddles two tensors), 16-byte accesses.  Skips
+// everything when the norm is not finite.
 __global__ __launch_bounds__(256) void adamw_kernel(
     float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
     float* __restrict__ v, bf16* __restrict__ shadow, int64_t n, float lr, float b1, float b2,
     float eps, float wd, float bc1, float bc2, const float* __restrict__ norm_scale, DecayMap dm) {
-  float nrm = norm_scale[0];
+  const float nrm = norm_scale[0];
   if (!isfinite(nrm)) return;
-  float scale = norm_scale[1];
-  int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const float scale = norm_scale[1];
+  const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i4 >= n) return;
-  float dec = decays(i4, dm) ? wd : 0.f;
-  int cnt = (int)min((int64_t)4, n - i4);
-  for (int j = 0; j < cnt; ++j) {
-    int64_t i = i4 + j;
-    float gi = g[i] * scale;
-    float mi = b1 * m[i] + (1.f - b1) * gi;
-    float vi = b2 * v[i] + (1.f - b2) * gi * gi;
-    m[i] = mi;
-    v[i] = vi;
-    float mhat = mi / bc1;
-    float vhat = vi / bc2;
-    float pi = p[i];
-    pi -= lr * (mhat / (sqrtf(vhat) + eps) + dec * pi);
-    p[i] = pi;
-    if (shadow) shadow[i] = (bf16)pi;
+  const float dec = decays(i4, dm) ? wd : 0.f;
+  if (i4 + 4 <= n) {
+    float4 pp = *reinterpret_cast<const float4*>(p + i4);
+    float4 gg = *reinterpret_cast<const float4*>(g + i4);
+    float4 mm = *reinterpret_cast<const float4*>(m + i4);
+    float4 vv = *reinterpret_cast<const float4*>(v + i4);
+    adamw_elem(pp.x, mm.x, vv.x, gg.x * scale, b1, b2, eps, dec, lr, bc1, bc2);
+    adamw_elem(pp.y, mm.y, vv.y, gg.y * scale, b1, b2, eps, dec, lr, bc1, bc2);
+    adamw_elem(pp.z, mm.z, vv.z, gg.z * scale, b1, b2, eps, dec, lr, bc1, bc2);
+    adamw_elem(pp.w, mm.w, vv.w, gg.w * scale, b1, b2, eps, dec, lr, bc1, bc2);
+    *reinterpret_cast<float4*>(p + i4) = pp;
+    *reinterpret_cast<float4*>(m + i4) = mm;
+    *reinterpret_cast<float4*>(v + i4) = vv;
+    if (shadow) {
+      union {
+        uint2 u;
+        bf16 e[4];
+      } w;
+      w.e[0] = (bf16)pp.x; w.e[1] = (bf16)pp.y; w.e[2] = (bf16)pp.z; w.e[3] = (bf16)pp.w;
+      *reinterpret_cast<uint2*>(shadow + i4) = w.u;
+    }
+  } else {
+    for (int64_t i = i4; i < n; ++i) {
+      float pi = p[i], mi = m[i], vi = v[i];
+      adamw_elem(pi, mi, vi, g[i] * scale, b1, b2, eps, dec, lr, bc1, bc2);
+      p[i] = pi;
+      m[i] = mi;
+      v[i] = vi;
+      if (shadow) shadow[i] = (bf16)pi;
+    }
   }
 }
 
@@ -618,9 +655,13 @@ hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int
 
 // =========================================================== fills / casts
 __global__ void fill_f32_kernel(float* __restrict__ p, float value, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+  const int64_t n4 = n / 4;
+  const float4 v4 = make_float4(value, value, value, value);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
        i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = value;
+    reinterpret_cast<float4*>(p)[i] = v4;
+  if (blockIdx.x == 0)
+    for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += blockDim.x) p[i] = value;
 }
 __global__ void fill_i32_kernel(int32_t* __restrict__ p, int32_t value, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;

@@ -18,6 +18,8 @@
 // 128 x 128 x 64, four waves of 64 x 64 (2 x 2 MFMA tiles), next k-tile
 // prefetched into registers while the current one is multiplied.
 // fp32 (the fp32 parity mode): plain LDS-tiled FMA kernel.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -246,39 +248,449 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K,
     }
 }
 
-// ================================================================ dispatch
+// ================================================================ bf16 MFMA, large tiles
+// Workgroup tile BM x BN (256 x 256 or 256 x 128) x 64, four waves of
+// (BM/2) x (BN/2).  Two LDS stages: while the waves multiply stage s, the
+// next k-tile (already in registers) is written to stage s^1 and the one
+// after is fetched from global memory, with one barrier per k-tile.  LDS
+// rows are 64 bf16 (128 B) with the 16-byte chunks XOR-swizzled by row, so
+// both the fragment reads and the transposing stores stay (nearly) free of
+// bank conflicts.  Workgroups are mapped XCD-major, then in groups of 8
+// tile-rows, so that concurrently running tiles share operands in L2.
+// gridDim.y > 1 splits K; with EPI_PARTIAL each split writes its fp32 tile
+// to out + split * M * N and splitk_reduce adds them in order.
+// Epilogue on 8 consecutive columns n .. n+7 of row m (16-byte accesses when
+// the row pitches allow it, element-wise at the ragged right edge).
 template <int MODE>
-static hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const void* A,
-                              int64_t lda, const void* B, int64_t ldb, const Epilogue& e,
-                              hipStream_t s) {
+__device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int N, const float* v,
+                                           int split, int M) {
+  if constexpr (MODE == EPI_PARTIAL) {
+    float* o = (float*)e.out + (int64_t)split * M * N + (int64_t)m * N + n;
+    if (n + 8 <= N && (N & 3) == 0) {
+      *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      for (int j = 0; j < 8 && n + j < N; ++j) o[j] = v[j];
+    }
+    return;
+  } else {
+    const bool vec = n + 8 <= N && (e.ldo & 7) == 0 && (e.ldr & 7) == 0 && (e.ldo2 & 7) == 0 &&
+                     (e.ldx & 7) == 0;
+    if (!vec) {
+      for (int j = 0; j < 8 && n + j < N; ++j) epi_apply<MODE, bf16>(e, m, n + j, v[j]);
+      return;
+    }
+    if constexpr (MODE == EPI_ACC_F32) {
+      float* o = (float*)e.out + (int64_t)m * e.ldo + n;
+      float4 a = *reinterpret_cast<float4*>(o), b = *reinterpret_cast<float4*>(o + 4);
+      a.x += v[0]; a.y += v[1]; a.z += v[2]; a.w += v[3];
+      b.x += v[4]; b.y += v[5]; b.z += v[6]; b.w += v[7];
+      *reinterpret_cast<float4*>(o) = a;
+      *reinterpret_cast<float4*>(o + 4) = b;
+    } else {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = v[j];
+      if constexpr (MODE == EPI_BIAS || MODE == EPI_BIAS_RESID || MODE == EPI_BIAS_GELU) {
+        float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
+        float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
+        x[0] += b0.x; x[1] += b0.y; x[2] += b0.z; x[3] += b0.w;
+        x[4] += b1.x; x[5] += b1.y; x[6] += b1.z; x[7] += b1.w;
+      }
+      if constexpr (MODE == EPI_BIAS_RESID) {
+        Pack<bf16> r = load_pack((const bf16*)e.resid + (int64_t)m * e.ldr + n);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] += to_f(r.e[j]);
+      }
+      if constexpr (MODE == EPI_GELU_BWD) {
+        Pack<bf16> h = load_pack((const bf16*)e.aux + (int64_t)m * e.ldx + n);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] *= gelu_grad_f(to_f(h.e[j]));
+      }
+      Pack<bf16> o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o.e[j] = (bf16)x[j];
+      store_pack((bf16*)e.out + (int64_t)m * e.ldo + n, o);
+      if constexpr (MODE == EPI_BIAS_GELU) {
+        Pack<bf16> g2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g2.e[j] = (bf16)gelu_f(to_f(o.e[j]));
+        store_pack((bf16*)e.out2 + (int64_t)m * e.ldo2 + n, g2);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int r, int chunk) { return r * 64 + ((chunk ^ swz(r)) << 3); }
+
+constexpr int BIG_THREADS = 512;  // 8 waves: 4 along M x 2 along N
+
+template <int R, bool KMAJOR>
+struct BigStage {
+  static constexpr int NV = R / 64;  // 16-byte vectors per thread per operand tile (R x 64)
+  uint4 v[NV];
+
+  // k-major: chunk c = tid + 512 i covers row c/8, k = (c%8)*8 .. +8
+  // m-major: thread covers KR consecutive k-rows x 8 consecutive rows
+  static constexpr int MC = R / 8;
+  static constexpr int KR = 64 / (BIG_THREADS / MC);
+
+  __device__ __forceinline__ void load(const bf16* __restrict__ P, int64_t ld, int row0,
+                                       int rows_total, int k0, int kend) {
+    if constexpr (KMAJOR) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        int c = threadIdx.x + BIG_THREADS * i;
+        int row = c >> 3, gk = k0 + (c & 7) * 8, gr = row0 + row;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (gr < rows_total && gk < kend) {
+          x = *reinterpret_cast<const uint4*>(P + (int64_t)gr * ld + gk);
+          if (gk + 8 > kend) {
+            Pack<bf16> pk;
+            pk.u = x;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (gk + j >= kend) pk.e[j] = (bf16)0.f;
+            x = pk.u;
+          }
+        }
+        v[i] = x;
+      }
+    } else {
+      int mc = threadIdx.x % MC, kg = threadIdx.x / MC;
+      int gr = row0 + mc * 8;
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        int gk = k0 + kg * KR + j;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (gk < kend && gr < rows_total) x = *reinterpret_cast<const uint4*>(P + (int64_t)gk * ld + gr);
+        v[j] = x;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(bf16* __restrict__ S) const {
+    if constexpr (KMAJOR) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        int c = threadIdx.x + BIG_THREADS * i;
+        *reinterpret_cast<uint4*>(S + lds_off(c >> 3, c & 7)) = v[i];
+      }
+    } else {
+      int mc = threadIdx.x % MC, kg = threadIdx.x / MC;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int row = mc * 8 + i, sh = (i & 1) * 16;
+        uint32_t e[KR];
+#pragma unroll
+        for (int j = 0; j < KR; ++j) e[j] = (reinterpret_cast<const uint32_t*>(&v[j])[i >> 1] >> sh) & 0xffffu;
+        // k = kg*KR .. +KR lands in chunk (kg*KR)/8 at element offset (kg*KR)%8
+        bf16* dst = S + lds_off(row, (kg * KR) >> 3) + ((kg * KR) & 7);
+        if constexpr (KR == 4) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = e[0] | (e[1] << 16);
+        }
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  // XCD-major renumbering: consecutive workgroup ids go round-robin over the 8 XCDs
+  const int nx = 8;
+  int xcd = bid % nx, local = bid / nx;
+  int per = (nblocks + nx - 1) / nx;
+  int tall = nblocks % nx;
+  int pid;
+  if (tall == 0 || xcd < tall) pid = xcd * per + local;
+  else pid = tall * per + (xcd - tall) * (per - 1) + local;
+  // grouped order: 8 tile-rows at a time, column-major inside a group
+  const int G = 8;
+  int in_group = G * tiles_n;
+  int group = pid / in_group;
+  int first_m = group * G;
+  int gsize = min(tiles_m - first_m, G);
+  int r = pid % in_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
+
+template <int BM, int BN, bool AKM, bool BKM, int MODE>
+__global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int K,
+                                                               const bf16* __restrict__ A, int64_t lda,
+                                                               const bf16* __restrict__ B, int64_t ldb,
+                                                               Epilogue e, int kps, int tiles_m,
+                                                               int tiles_n) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * 64];
+  constexpr int WM = BM / 4, WN = BN / 2, TI = WM / 32, TJ = WN / 32;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
+  const int wm = wave / 2, wn = wave % 2;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = blockIdx.y * kps;
+  const int kend = min(K, kbeg + kps);
+  const int nk = kend > kbeg ? (int)cdiv(kend - kbeg, 64) : 0;
+
+  f32x16_t acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // NST register stages: tile t lives in stage t % NST from its global load
+  // (issued NST k-tiles ahead of its use) until its LDS store.  256 x 128
+  // tiles afford two stages within 256 registers per lane; 256 x 256 one.
+  constexpr int NST = BN == 256 ? 1 : 2;
+  BigStage<BM, AKM> sa[NST];
+  BigStage<BN, BKM> sb[NST];
+  auto As = [&](int buf) { return smem + buf * BM * 64; };
+  auto Bs = [&](int buf) { return smem + 2 * BM * 64 + buf * BN * 64; };
+
+  if (nk > 0) {
+    sa[0].load(A, lda, m0, M, kbeg, kend);
+    sb[0].load(B, ldb, n0, N, kbeg, kend);
+    if constexpr (NST == 2) {
+      if (nk > 1) {
+        sa[NST - 1].load(A, lda, m0, M, kbeg + 64, kend);
+        sb[NST - 1].load(B, ldb, n0, N, kbeg + 64, kend);
+      }
+    }
+    sa[0].store(As(0));
+    sb[0].store(Bs(0));
+    if (nk > NST) {
+      sa[0].load(A, lda, m0, M, kbeg + NST * 64, kend);
+      sb[0].load(B, ldb, n0, N, kbeg + NST * 64, kend);
+    }
+  }
+  __syncthreads();
+
+  auto mma_tile = [&](int buf) {
+    const bf16* a_s = As(buf);
+    const bf16* b_s = Bs(buf);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t a[TI];
+      const int chunk = s * 2 + h2;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(a_s + lds_off(wm * WM + i * 32 + l32, chunk));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(b_s + lds_off(wn * WN + j * 32 + l32, chunk));
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  // iteration kt: store tile kt+1 (register stage (kt+1) % NST) to LDS buffer
+  // (kt+1) % 2, refill that register stage with tile kt+1+NST, multiply tile kt.
+  auto step = [&](int kt, auto lb_c) {
+    constexpr int lb = decltype(lb_c)::value;  // == (kt + 1) % 2
+    constexpr int st = lb % NST;
+    if (kt + 1 < nk) {
+      sa[st].store(As(lb));
+      sb[st].store(Bs(lb));
+      if (kt + 1 + NST < nk) {
+        sa[st].load(A, lda, m0, M, kbeg + (kt + 1 + NST) * 64, kend);
+        sb[st].load(B, ldb, n0, N, kbeg + (kt + 1 + NST) * 64, kend);
+      }
+    }
+    mma_tile(lb ^ 1);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 1>());
+    step(kt + 1, std::integral_constant<int, 0>());
+  }
+  if (kt < nk) step(kt, std::integral_constant<int, 1>());
+
+  // Epilogue through LDS: each wave stages 16 rows x WN of fp32 at a time
+  // (the accumulator layout spreads a row over 32 lanes) and reads them back
+  // as 8 consecutive columns per lane for 16-byte global accesses.
+  constexpr int SP = WN + 4;
+  float* stage = reinterpret_cast<float*>(smem) + wave * 16 * SP;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          const int r = 8 * half + rr;
+          stage[(8 * (rr / 4) + 4 * h2 + (rr % 4)) * SP + j * 32 + l32] = acc[i][j][r];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < WN / 32; ++q) {
+        const int c = lane + 64 * q;
+        const int row = c / (WN / 8), col = (c % (WN / 8)) * 8;
+        const float4 a = *reinterpret_cast<const float4*>(stage + row * SP + col);
+        const float4 b = *reinterpret_cast<const float4*>(stage + row * SP + col + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const int m = m0 + wm * WM + i * 32 + 16 * half + row, n = n0 + wn * WN + col;
+        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// dst[m, n] (fp32, row pitch ldo) += sum over s of part[s][m][n], in order.
+__global__ void splitk_reduce_kernel(float* __restrict__ dst, int64_t ldo,
+                                     const float* __restrict__ part, int S, int M, int N) {
+  int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  int64_t total = (int64_t)M * N;
+  if (idx >= total) return;
+  int m = (int)(idx / N), n = (int)(idx % N);
+  float4 acc = *reinterpret_cast<const float4*>(part + idx);
+  for (int s = 1; s < S; ++s) {
+    float4 p = *reinterpret_cast<const float4*>(part + (int64_t)s * total + idx);
+    acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+  }
+  float4* d = reinterpret_cast<float4*>(dst + (int64_t)m * ldo + n);
+  float4 o = *d;
+  o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+  *d = o;
+}
+
+// ================================================================ dispatch
+namespace {
+
+constexpr int kCUs = 256;
+
+struct Plan {
+  int kind;  // 0: 128x128 kernel, 1: 256x256, 2: 256x128
+  int splits;
+};
+
+// 256 x 256 tiles need all 512 registers for the accumulators and operand
+// staging; the GELU epilogues would spill there, so they use 256 x 128.
+constexpr bool big_square_ok(int mode) { return mode != EPI_BIAS_GELU && mode != EPI_GELU_BWD; }
+
+Plan plan_gemm(int M, int N, int K, int mode) {
+  if (M < 256 || N < 128) return {0, 1};
+  const int cand[2][3] = {{1, 256, 256}, {2, 256, 128}};
+  const double eff[3] = {0.0, 1.0, 0.8};
+  Plan best{2, 1};
+  double best_t = 1e300;
+  for (auto& c : cand) {
+    if (c[0] == 1 && !big_square_ok(mode)) continue;
+    int bm = c[1], bn = c[2];
+    int64_t tiles = cdiv(M, bm) * cdiv(N, bn);
+    int S = 1;
+    if (mode == EPI_ACC_F32 && tiles < kCUs && K >= 2048) {
+      S = (int)(kCUs / tiles);
+      S = S > 16 ? 16 : S;
+      int maxs = K / 1024;
+      S = S > maxs ? maxs : S;
+      S = S < 1 ? 1 : S;
+    }
+    int64_t rounds = cdiv(tiles * S, kCUs);
+    double t = (double)rounds * bm * bn * (double)cdiv(K, S) / eff[c[0]];
+    if (t < best_t) {
+      best_t = t;
+      best = {c[0], S};
+    }
+  }
+  return best;
+}
+
+template <int BM, int BN, int MODE>
+hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, int64_t lda,
+                      const bf16* b, int64_t ldb, const Epilogue& e, int splits, hipStream_t s) {
+  int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
+  int kps = (int)round_up(cdiv(K, splits), 64);
+  dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
+#define GO(AK, BK_) gemm_big_kernel<BM, BN, AK, BK_, MODE><<<grid, BIG_THREADS, 0, s>>>(M, N, K, a, lda, b, ldb, e, kps, tiles_m, tiles_n)
+  if (akm && bkm) GO(true, true);
+  else if (akm && !bkm) GO(true, false);
+  else if (!akm && !bkm) GO(false, false);
+  else GO(false, true);
+#undef GO
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, const Epilogue& e, hipStream_t s, void* ws,
+                       size_t ws_bytes) {
   if (dt == F32) {
     dim3 grid((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64));
     gemm_simt_kernel<MODE><<<grid, 256, 0, s>>>(akm, bkm, M, N, K, (const float*)A, lda,
                                                  (const float*)B, ldb, e);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)cdiv(N, MF_BN), (unsigned)cdiv(M, MF_BM));
   const bf16* a = (const bf16*)A;
   const bf16* b = (const bf16*)B;
-  if (akm && bkm) gemm_mfma_kernel<true, true, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
-  else if (akm && !bkm) gemm_mfma_kernel<true, false, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
-  else if (!akm && !bkm) gemm_mfma_kernel<false, false, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
-  else gemm_mfma_kernel<false, true, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
-  return hipGetLastError();
+  Plan p = plan_gemm(M, N, K, MODE);
+  if (p.kind == 0) {
+    dim3 grid((unsigned)cdiv(N, MF_BN), (unsigned)cdiv(M, MF_BM));
+    if (akm && bkm) gemm_mfma_kernel<true, true, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
+    else if (akm && !bkm) gemm_mfma_kernel<true, false, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
+    else if (!akm && !bkm) gemm_mfma_kernel<false, false, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
+    else gemm_mfma_kernel<false, true, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
+    return hipGetLastError();
+  }
+  if constexpr (MODE == EPI_ACC_F32) {
+    if (p.splits > 1) {
+      size_t need = (size_t)p.splits * M * N * sizeof(float);
+      if (!ws || ws_bytes < need || N % 4 != 0 || e.ldo % 4 != 0) {
+        p.splits = 1;  // not enough scratch: run unsplit
+      } else {
+        Epilogue pe = e;
+        pe.mode = EPI_PARTIAL;
+        pe.out = ws;
+        hipError_t err = p.kind == 1
+            ? launch_big<256, 256, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s)
+            : launch_big<256, 128, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s);
+        if (err != hipSuccess) return err;
+        int64_t n4 = (int64_t)M * N / 4;
+        splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, s>>>((float*)e.out, e.ldo,
+                                                                    (const float*)ws, p.splits, M, N);
+        return hipGetLastError();
+      }
+    }
+  }
+  if constexpr (big_square_ok(MODE)) {
+    if (p.kind == 1) return launch_big<256, 256, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
+  }
+  return launch_big<256, 128, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode) {
+  if (dt != BF16 || mode != EPI_ACC_F32) return 0;
+  Plan p = plan_gemm(M, N, K, mode);
+  if (p.kind == 0 || p.splits <= 1) return 0;
+  return (size_t)p.splits * M * N * sizeof(float);
 }
 
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
-                int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s) {
+                int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
+                void* ws, size_t ws_bytes) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dt == BF16 && (lda % 8 != 0 || ldb % 8 != 0)) return hipErrorInvalidValue;
+#define CASE(MD) \
+  case MD: return launch_mode<MD>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s, ws, ws_bytes);
   switch (e.mode) {
-    case EPI_STORE: return launch_mode<EPI_STORE>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s);
-    case EPI_BIAS: return launch_mode<EPI_BIAS>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s);
-    case EPI_BIAS_RESID: return launch_mode<EPI_BIAS_RESID>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s);
-    case EPI_BIAS_GELU: return launch_mode<EPI_BIAS_GELU>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s);
-    case EPI_GELU_BWD: return launch_mode<EPI_GELU_BWD>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s);
-    case EPI_ACC_F32: return launch_mode<EPI_ACC_F32>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s);
+    CASE(EPI_STORE)
+    CASE(EPI_BIAS)
+    CASE(EPI_BIAS_RESID)
+    CASE(EPI_BIAS_GELU)
+    CASE(EPI_GELU_BWD)
+    CASE(EPI_ACC_F32)
   }
+#undef CASE
   return hipErrorInvalidValue;
 }
 

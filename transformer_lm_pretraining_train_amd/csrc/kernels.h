@@ -64,7 +64,8 @@ enum EpiMode {
   EPI_BIAS_RESID = 2,  // out = acc + bias[n] + resid[m, n]
   EPI_BIAS_GELU = 3,   // out = acc + bias[n]; out2 = gelu(out)
   EPI_GELU_BWD = 4,    // out = acc * gelu'(aux[m, n])
-  EPI_ACC_F32 = 5      // out (fp32) += acc
+  EPI_ACC_F32 = 5,     // out (fp32) += acc
+  EPI_PARTIAL = 6      // internal: split-K partial tile, fp32
 };
 struct Epilogue {
   int mode;
@@ -78,8 +79,12 @@ struct Epilogue {
   const void* aux;
   int64_t ldx;
 };
+// Split-K (used for fp32-accumulating products with few output tiles and a
+// long K) needs gemm_workspace_bytes() of scratch in `ws`.
+size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode);
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
-                int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s);
+                int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
+                void* ws = nullptr, size_t ws_bytes = 0);
 
 // ---- optimizer
 struct DecayMap {  // which flat elements belong to 2-D tensors

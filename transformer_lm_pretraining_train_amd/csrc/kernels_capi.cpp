@@ -24,7 +24,7 @@ extern "C" {
 int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const void* A,
                int64_t lda, const void* B, int64_t ldb, int epilogue, void* out, int64_t ldo,
                const float* bias, const void* resid, int64_t ldr, void* out2, int64_t ldo2,
-               const void* aux, int64_t ldx, void* stream) {
+               const void* aux, int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
   if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
     return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
   if (M < 0 || N < 0 || K < 0 || !A || !B || !out)
@@ -49,8 +49,12 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
   e.aux = aux;
   e.ldx = ldx;
   return launch_rc(gemm(dtype, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb, e,
-                        (hipStream_t)stream),
+                        (hipStream_t)stream, ws, ws_bytes),
                    "gemm");
+}
+
+size_t gpt2k_gemm_workspace_bytes(int dtype, int M, int N, int K, int epilogue) {
+  return gemm_workspace_bytes(dtype, M, N, K, epilogue);
 }
 
 int gpt2k_attention_forward(int dtype, void* out, float* lse, const void* qkv, int B, int T, int H,

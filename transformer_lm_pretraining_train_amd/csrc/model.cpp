@@ -155,6 +155,8 @@ struct gpt2_model {
   // backward
   void *dres, *dbuf_c, *dbuf_4c, *dqkv;
   void* scratch;
+  void* gemm_ws;  // split-K partial tiles of the weight-gradient GEMMs
+  size_t gemm_ws_bytes;
   void* norm_scratch;
   int* err_flag;
   // bookkeeping
@@ -232,6 +234,15 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   sc = std::max(sc, bias_grad_scratch_bytes((int)M, (int)(4 * C)));
   sc = std::max(sc, attention_backward_scratch_bytes(c.micro_batch, c.seq_len, H));
   md.scratch = cv.take(sc);
+  size_t gw = 0;
+  {
+    const int Mi = (int)M, Ci = (int)C;
+    const int dWshapes[5][2] = {{c.padded_vocab_size, Ci}, {Ci, 4 * Ci}, {4 * Ci, Ci}, {Ci, Ci},
+                                {3 * Ci, Ci}};
+    for (auto& sh : dWshapes) gw = std::max(gw, gemm_workspace_bytes(dt, sh[0], sh[1], Mi, EPI_ACC_F32));
+  }
+  md.gemm_ws = gw ? cv.take(gw) : nullptr;
+  md.gemm_ws_bytes = gw;
   md.norm_scratch = cv.take(grad_norm_scratch_bytes());
   md.err_flag = (int*)cv.take(4);
   return (cv.off + kAlign - 1) / kAlign * kAlign;
@@ -493,7 +504,7 @@ int gpt2_backward(gpt2_model* md) {
   LAUNCH(crossentropy_backward(dt, md->logits, md->ldl, md->ce_lse, md->targets, M, md->V, seed, s));
   // tied head: dwte += dz^T lnf ; dlnf = dz wte
   LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->logits, md->ldl, md->lnf, C,
-              epi(EPI_ACC_F32, G + Ly.wte, C), s));
+              epi(EPI_ACC_F32, G + Ly.wte, C), s, md->gemm_ws, md->gemm_ws_bytes));
   LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->logits, md->ldl, md->wt(Ly.wte), C,
               epi(EPI_STORE, md->dbuf_c, C), s));
   const void* xfinal = md->L > 0 ? md->act[md->L - 1].res3 : md->encoded;
@@ -506,7 +517,7 @@ int gpt2_backward(gpt2_model* md) {
     const void* xin = l > 0 ? md->act[l - 1].res3 : md->encoded;
     // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
     LAUNCH(gemm(dt, false, false, C, 4 * C, M, md->dres, C, a.fchg, 4 * C,
-                epi(EPI_ACC_F32, G + o.fcp_w, 4 * C), s));
+                epi(EPI_ACC_F32, G + o.fcp_w, 4 * C), s, md->gemm_ws, md->gemm_ws_bytes));
     LAUNCH(bias_grad(dt, G + o.fcp_b, md->dres, M, C, C, md->scratch, s));
     Epilogue e = epi(EPI_GELU_BWD, md->dbuf_4c, 4 * C);
     e.aux = a.fch;
@@ -514,7 +525,7 @@ int gpt2_backward(gpt2_model* md) {
     LAUNCH(gemm(dt, true, false, M, 4 * C, C, md->dres, C, md->wt(o.fcp_w), 4 * C, e, s));
     // fc: fch = ln2 fc_w^T + fc_b  (dbuf_4c now holds d fch)
     LAUNCH(gemm(dt, false, false, 4 * C, C, M, md->dbuf_4c, 4 * C, a.ln2, C,
-                epi(EPI_ACC_F32, G + o.fc_w, C), s));
+                epi(EPI_ACC_F32, G + o.fc_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
     LAUNCH(bias_grad(dt, G + o.fc_b, md->dbuf_4c, M, 4 * C, 4 * C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, 4 * C, md->dbuf_4c, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
@@ -522,7 +533,7 @@ int gpt2_backward(gpt2_model* md) {
                               a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C, md->scratch, s));
     // attention output projection: res2 = x + atty proj_w^T + proj_b
     LAUNCH(gemm(dt, false, false, C, C, M, md->dres, C, a.atty, C,
-                epi(EPI_ACC_F32, G + o.proj_w, C), s));
+                epi(EPI_ACC_F32, G + o.proj_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
     LAUNCH(bias_grad(dt, G + o.proj_b, md->dres, M, C, C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, C, md->dres, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
@@ -530,7 +541,7 @@ int gpt2_backward(gpt2_model* md) {
                               md->hd, md->scratch, s));
     // qkv = ln1 qkv_w^T + qkv_b
     LAUNCH(gemm(dt, false, false, 3 * C, C, M, md->dqkv, 3 * C, a.ln1, C,
-                epi(EPI_ACC_F32, G + o.qkv_w, C), s));
+                epi(EPI_ACC_F32, G + o.qkv_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
     LAUNCH(bias_grad(dt, G + o.qkv_b, md->dqkv, M, 3 * C, 3 * C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, 3 * C, md->dqkv, 3 * C, md->wt(o.qkv_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
