@@ -86,7 +86,8 @@ EPIS = ["store", "bias", "bias_resid", "bias_gelu", "gelu_bwd", "acc_f32"]
 
 @pytest.mark.parametrize("dt", [FP32, BF16])
 @pytest.mark.parametrize("akm,bkm", ORIENT)
-@pytest.mark.parametrize("M,N,K", [(200, 72, 136), (129, 65, 65), (256, 128, 64), (64, 320, 1000)])
+@pytest.mark.parametrize("M,N,K", [(200, 72, 136), (129, 65, 65), (256, 128, 64), (64, 320, 1000),
+                                   (300, 200, 136), (777, 1000, 520), (512, 129, 65), (1024, 768, 192)])
 def test_gemm_orientations_ragged(dt, akm, bkm, M, N, K):
     print(f"gemm dt={dt} akm={akm} bkm={bkm} M={M} N={N} K={K}", flush=True)
     r = run_gemm(dt, akm, bkm, M, N, K, "store", seed=M + N + K, ld_extra=8)
@@ -101,6 +102,10 @@ def test_gemm_epilogues(dt, epi):
     print(f"gemm epilogue dt={dt} {epi}", flush=True)
     akm, bkm = (False, False) if epi == "acc_f32" else (True, True)
     r = run_gemm(dt, akm, bkm, 150, 136, 200, epi, seed=3)
+    tol = 1e-5 if dt == FP32 or epi == "acc_f32" else 4e-3
+    assert rel_l2(r["got"], r["expect"]) < tol
+    # the same epilogue on the large-tile kernels (M >= 256), ragged edges
+    r = run_gemm(dt, akm, bkm, 520, 392, 200, epi, seed=4)
     tol = 1e-5 if dt == FP32 or epi == "acc_f32" else 4e-3
     assert rel_l2(r["got"], r["expect"]) < tol
     if epi == "bias_gelu":

@@ -326,24 +326,30 @@ __device__ __forceinline__ int lds_off(int r, int chunk) { return r * 64 + ((chu
 
 constexpr int BIG_THREADS = 512;  // 8 waves: 4 along M x 2 along N
 
-template <int R, bool KMAJOR>
-struct BigStage {
-  static constexpr int NV = R / 64;  // 16-byte vectors per thread per operand tile (R x 64)
-  uint4 v[NV];
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-  // k-major: chunk c = tid + 512 i covers row c/8, k = (c%8)*8 .. +8
-  // m-major: thread covers KR consecutive k-rows x 8 consecutive rows
-  static constexpr int MC = R / 8;
-  static constexpr int KR = 64 / (BIG_THREADS / MC);
+// LDS image of one operand tile (R rows of the output dimension x 64 k).
+//  k-major source: [row][64 k], 128-byte rows, 16-byte chunks XOR-swizzled
+//    by row; fragments are single 16-byte reads.
+//  m-major source: [64 k][R rows] exactly as in memory, row pitch R + 32
+//    elements (so that a 32-lane half of a transposing read touches 8
+//    distinct 32-byte bank groups); fragments are two ds_read_b64_tr_b16
+//    reads (each lane gets 4 consecutive k of its row).
+template <int R, bool KMAJOR>
+struct BigOperand {
+  static constexpr int PITCH = KMAJOR ? 64 : R + 32;
+  static constexpr int ELEMS = KMAJOR ? R * 64 : 64 * PITCH;
+  static constexpr int NV = R / 64;  // 16-byte vectors per thread per tile
+  uint4 v[NV];
 
   __device__ __forceinline__ void load(const bf16* __restrict__ P, int64_t ld, int row0,
                                        int rows_total, int k0, int kend) {
-    if constexpr (KMAJOR) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        int c = threadIdx.x + BIG_THREADS * i;
-        int row = c >> 3, gk = k0 + (c & 7) * 8, gr = row0 + row;
-        uint4 x = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < NV; ++i) {
+      const int c = threadIdx.x + BIG_THREADS * i;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if constexpr (KMAJOR) {
+        const int row = c >> 3, gk = k0 + (c & 7) * 8, gr = row0 + row;
         if (gr < rows_total && gk < kend) {
           x = *reinterpret_cast<const uint4*>(P + (int64_t)gr * ld + gk);
           if (gk + 8 > kend) {
@@ -355,44 +361,43 @@ struct BigStage {
             x = pk.u;
           }
         }
-        v[i] = x;
-      }
-    } else {
-      int mc = threadIdx.x % MC, kg = threadIdx.x / MC;
-      int gr = row0 + mc * 8;
-#pragma unroll
-      for (int j = 0; j < KR; ++j) {
-        int gk = k0 + kg * KR + j;
-        uint4 x = make_uint4(0, 0, 0, 0);
+      } else {
+        const int krow = c / (R / 8), gr = row0 + (c % (R / 8)) * 8, gk = k0 + krow;
         if (gk < kend && gr < rows_total) x = *reinterpret_cast<const uint4*>(P + (int64_t)gk * ld + gr);
-        v[j] = x;
       }
+      v[i] = x;
     }
   }
 
   __device__ __forceinline__ void store(bf16* __restrict__ S) const {
-    if constexpr (KMAJOR) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        int c = threadIdx.x + BIG_THREADS * i;
+    for (int i = 0; i < NV; ++i) {
+      const int c = threadIdx.x + BIG_THREADS * i;
+      if constexpr (KMAJOR) {
         *reinterpret_cast<uint4*>(S + lds_off(c >> 3, c & 7)) = v[i];
+      } else {
+        *reinterpret_cast<uint4*>(S + (c / (R / 8)) * PITCH + (c % (R / 8)) * 8) = v[i];
       }
+    }
+  }
+
+  // MFMA operand: lane holds row `row0 + lane%32`, k = ks*16 + 8*h2 .. +8.
+  __device__ __forceinline__ static bf16x8_t frag(const bf16* S, int row0, int ks, int lane) {
+    const int h2 = lane >> 5;
+    if constexpr (KMAJOR) {
+      return *reinterpret_cast<const bf16x8_t*>(S + lds_off(row0 + (lane & 31), ks * 2 + h2));
     } else {
-      int mc = threadIdx.x % MC, kg = threadIdx.x / MC;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int row = mc * 8 + i, sh = (i & 1) * 16;
-        uint32_t e[KR];
-#pragma unroll
-        for (int j = 0; j < KR; ++j) e[j] = (reinterpret_cast<const uint32_t*>(&v[j])[i >> 1] >> sh) & 0xffffu;
-        // k = kg*KR .. +KR lands in chunk (kg*KR)/8 at element offset (kg*KR)%8
-        bf16* dst = S + lds_off(row, (kg * KR) >> 3) + ((kg * KR) & 7);
-        if constexpr (KR == 4) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = e[0] | (e[1] << 16);
-        }
-      }
+      const int j = lane & 15;
+      const int col = row0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const bf16* p = S + (ks * 16 + 8 * h2 + (j >> 2)) * PITCH + col;
+      union {
+        v4i16 s[2];
+        bf16x8_t v;
+      } r;
+      r.s[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+      r.s[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(p + 4 * PITCH));
+      return r.v;
     }
   }
 };
@@ -418,13 +423,24 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
   tn = r / gsize;
 }
 
+template <int BM, int BN, bool AKM, bool BKM>
+struct BigSmem {
+  using OA = BigOperand<BM, AKM>;
+  using OB = BigOperand<BN, BKM>;
+  static constexpr int STAGE = OA::ELEMS + OB::ELEMS;
+  static constexpr int ELEMS = 2 * STAGE;
+};
+
 template <int BM, int BN, bool AKM, bool BKM, int MODE>
 __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int K,
                                                                const bf16* __restrict__ A, int64_t lda,
                                                                const bf16* __restrict__ B, int64_t ldb,
                                                                Epilogue e, int kps, int tiles_m,
                                                                int tiles_n) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * 64];
+  using SM = BigSmem<BM, BN, AKM, BKM>;
+  using OA = typename SM::OA;
+  using OB = typename SM::OB;
+  __shared__ __attribute__((aligned(16))) bf16 smem[SM::ELEMS];
   constexpr int WM = BM / 4, WN = BN / 2, TI = WM / 32, TJ = WN / 32;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
   const int wm = wave / 2, wn = wave % 2;
@@ -444,13 +460,13 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // NST register stages: tile t lives in stage t % NST from its global load
-  // (issued NST k-tiles ahead of its use) until its LDS store.  256 x 128
-  // tiles afford two stages within 256 registers per lane; 256 x 256 one.
+  // (issued NST k-tiles ahead of its use) until its LDS store.  Tiles up to
+  // 256 x 192 afford two stages within 256 registers per lane; 256 x 256 one.
   constexpr int NST = BN == 256 ? 1 : 2;
-  BigStage<BM, AKM> sa[NST];
-  BigStage<BN, BKM> sb[NST];
-  auto As = [&](int buf) { return smem + buf * BM * 64; };
-  auto Bs = [&](int buf) { return smem + 2 * BM * 64 + buf * BN * 64; };
+  OA sa[NST];
+  OB sb[NST];
+  auto As = [&](int buf) { return smem + buf * SM::STAGE; };
+  auto Bs = [&](int buf) { return smem + buf * SM::STAGE + OA::ELEMS; };
 
   if (nk > 0) {
     sa[0].load(A, lda, m0, M, kbeg, kend);
@@ -476,13 +492,11 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t a[TI];
-      const int chunk = s * 2 + h2;
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(a_s + lds_off(wm * WM + i * 32 + l32, chunk));
+      for (int i = 0; i < TI; ++i) a[i] = OA::frag(a_s, wm * WM + i * 32, s, lane);
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(b_s + lds_off(wn * WN + j * 32 + l32, chunk));
+        const bf16x8_t b = OB::frag(b_s, wn * WN + j * 32, s, lane);
 #pragma unroll
         for (int i = 0; i < TI; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
@@ -516,6 +530,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
   // (the accumulator layout spreads a row over 32 lanes) and reads them back
   // as 8 consecutive columns per lane for 16-byte global accesses.
   constexpr int SP = WN + 4;
+  static_assert(8 * 16 * SP * 4 <= SM::ELEMS * 2, "epilogue staging exceeds LDS");
   float* stage = reinterpret_cast<float*>(smem) + wave * 16 * SP;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
@@ -529,15 +544,18 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
           stage[(8 * (rr / 4) + 4 * h2 + (rr % 4)) * SP + j * 32 + l32] = acc[i][j][r];
         }
       __syncthreads();
+      constexpr int CHUNKS = 16 * WN / 8;  // 8-column chunks in the slab
 #pragma unroll
-      for (int q = 0; q < WN / 32; ++q) {
+      for (int q = 0; q < (CHUNKS + 63) / 64; ++q) {
         const int c = lane + 64 * q;
-        const int row = c / (WN / 8), col = (c % (WN / 8)) * 8;
-        const float4 a = *reinterpret_cast<const float4*>(stage + row * SP + col);
-        const float4 b = *reinterpret_cast<const float4*>(stage + row * SP + col + 4);
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        const int m = m0 + wm * WM + i * 32 + 16 * half + row, n = n0 + wn * WN + col;
-        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
+        if (c < CHUNKS) {
+          const int row = c / (WN / 8), col = (c % (WN / 8)) * 8;
+          const float4 a = *reinterpret_cast<const float4*>(stage + row * SP + col);
+          const float4 b = *reinterpret_cast<const float4*>(stage + row * SP + col + 4);
+          const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          const int m = m0 + wm * WM + i * 32 + 16 * half + row, n = n0 + wn * WN + col;
+          if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
+        }
       }
       __syncthreads();
     }
@@ -568,7 +586,7 @@ namespace {
 constexpr int kCUs = 256;
 
 struct Plan {
-  int kind;  // 0: 128x128 kernel, 1: 256x256, 2: 256x128
+  int kind;  // 0: 128x128 kernel, 1: 256x256, 2: 256x128, 3: 256x192
   int splits;
 };
 
@@ -578,8 +596,9 @@ constexpr bool big_square_ok(int mode) { return mode != EPI_BIAS_GELU && mode !=
 
 Plan plan_gemm(int M, int N, int K, int mode) {
   if (M < 256 || N < 128) return {0, 1};
-  const int cand[2][3] = {{1, 256, 256}, {2, 256, 128}};
-  const double eff[3] = {0.0, 1.0, 0.8};
+  // kind: 1 = 256 x 256, 2 = 256 x 128, 3 = 256 x 192
+  const int cand[3][3] = {{1, 256, 256}, {3, 256, 192}, {2, 256, 128}};
+  const double eff[4] = {0.0, 1.0, 0.8, 0.92};
   Plan best{2, 1};
   double best_t = 1e300;
   for (auto& c : cand) {
@@ -649,9 +668,10 @@ hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const vo
         Epilogue pe = e;
         pe.mode = EPI_PARTIAL;
         pe.out = ws;
-        hipError_t err = p.kind == 1
-            ? launch_big<256, 256, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s)
-            : launch_big<256, 128, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s);
+        hipError_t err =
+            p.kind == 1 ? launch_big<256, 256, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s)
+            : p.kind == 3 ? launch_big<256, 192, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s)
+                          : launch_big<256, 128, EPI_PARTIAL>(akm, bkm, M, N, K, a, lda, b, ldb, pe, p.splits, s);
         if (err != hipSuccess) return err;
         int64_t n4 = (int64_t)M * N / 4;
         splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, s>>>((float*)e.out, e.ldo,
@@ -663,6 +683,7 @@ hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const vo
   if constexpr (big_square_ok(MODE)) {
     if (p.kind == 1) return launch_big<256, 256, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
   }
+  if (p.kind == 3) return launch_big<256, 192, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
   return launch_big<256, 128, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
 }
 
