@@ -328,56 +328,70 @@ constexpr int BIG_THREADS = 512;  // 8 waves: 4 along M x 2 along N
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// LDS image of one operand tile (R rows of the output dimension x 64 k).
-//  k-major source: [row][64 k], 128-byte rows, 16-byte chunks XOR-swizzled
-//    by row; fragments are single 16-byte reads.
-//  m-major source: [64 k][R rows] exactly as in memory, row pitch R + 32
-//    elements (so that a 32-lane half of a transposing read touches 8
-//    distinct 32-byte bank groups); fragments are two ds_read_b64_tr_b16
-//    reads (each lane gets 4 consecutive k of its row).
-template <int R, bool KMAJOR>
-struct BigOperand {
-  static constexpr int PITCH = KMAJOR ? 64 : R + 32;
-  static constexpr int ELEMS = KMAJOR ? R * 64 : 64 * PITCH;
-  static constexpr int NV = R / 64;  // 16-byte vectors per thread per tile
-  uint4 v[NV];
+// Source of the zero vectors that out-of-range operand loads read.
+__device__ __attribute__((aligned(16))) uint4 g_zero16[1] = {{0u, 0u, 0u, 0u}};
 
-  __device__ __forceinline__ void load(const bf16* __restrict__ P, int64_t ld, int row0,
-                                       int rows_total, int k0, int kend) {
+// One operand tile (R rows of the output dimension x 64 k) in LDS, filled
+// by direct global->LDS loads: one wave instruction writes 64 consecutive
+// 16-byte slots, lane i at slot i, and each lane fetches the global vector
+// that belongs in its slot.  No registers hold the tile in flight.
+//  k-major source: [row][64 k], 128-byte rows, 16-byte chunks XOR-swizzled
+//    by row (conflict-free 16-byte fragment reads).
+//  m-major source: [64 k][R rows] as in memory, the chunks of k-row k
+//    rotated by 4*(k%4) (so the four k-rows of a transposing read hit
+//    different banks); fragments via ds_read_b64_tr_b16.  R >= 128.
+template <int R, bool KMAJOR, int NW>
+struct BigOperand {
+  static constexpr int ELEMS = R * 64;
+  static constexpr int CPR = R / 8;     // 16-byte chunks per k-row (m-major)
+  static constexpr int NI = R * 8 / (64 * NW);  // load instructions per wave per tile
+
+  // physical chunk of logical chunk lc in k-row krow, and the inverse
+  __device__ __forceinline__ static int mphys(int krow, int lc) { return (lc + CPR - 4 * (krow & 3)) % CPR; }
+  __device__ __forceinline__ static int mlog(int krow, int p) { return (p + 4 * (krow & 3)) % CPR; }
+
+  // Per-lane source of each of the NI load instructions, fixed for the whole
+  // k loop: the vector at k-offset kofs[q] (relative to a tile's first k)
+  // of a row that is in range (rok) or not.
+  struct Src {
+    const bf16* p[NI];
+    int kofs[NI];
+    bool rok[NI];
+  };
+
+  __device__ __forceinline__ static void init(Src& st, const bf16* __restrict__ P, int64_t ld,
+                                              int row0, int rows_total, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c = threadIdx.x + BIG_THREADS * i;
-      uint4 x = make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < NI; ++q) {
+      const int slot = (wave + NW * q) * 64 + lane;
+      int gr, ko;
       if constexpr (KMAJOR) {
-        const int row = c >> 3, gk = k0 + (c & 7) * 8, gr = row0 + row;
-        if (gr < rows_total && gk < kend) {
-          x = *reinterpret_cast<const uint4*>(P + (int64_t)gr * ld + gk);
-          if (gk + 8 > kend) {
-            Pack<bf16> pk;
-            pk.u = x;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (gk + j >= kend) pk.e[j] = (bf16)0.f;
-            x = pk.u;
-          }
-        }
+        const int row = slot >> 3;
+        gr = row0 + row;
+        ko = 8 * ((slot & 7) ^ swz(row));
+        st.p[q] = P + (int64_t)gr * ld + ko;
       } else {
-        const int krow = c / (R / 8), gr = row0 + (c % (R / 8)) * 8, gk = k0 + krow;
-        if (gk < kend && gr < rows_total) x = *reinterpret_cast<const uint4*>(P + (int64_t)gk * ld + gr);
+        const int krow = slot / CPR;
+        gr = row0 + 8 * mlog(krow, slot % CPR);
+        ko = krow;
+        st.p[q] = P + (int64_t)krow * ld + gr;
       }
-      v[i] = x;
+      st.kofs[q] = ko;
+      st.rok[q] = gr < rows_total;
     }
   }
 
-  __device__ __forceinline__ void store(bf16* __restrict__ S) const {
+  // Issue the direct loads of the tile starting at k0 into LDS tile S.
+  __device__ __forceinline__ static void load(bf16* __restrict__ S, const Src& st, int64_t ld,
+                                              int k0, int kend, int wave, int lane) {
+    const int64_t kstep = KMAJOR ? (int64_t)k0 : (int64_t)k0 * ld;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int c = threadIdx.x + BIG_THREADS * i;
-      if constexpr (KMAJOR) {
-        *reinterpret_cast<uint4*>(S + lds_off(c >> 3, c & 7)) = v[i];
-      } else {
-        *reinterpret_cast<uint4*>(S + (c / (R / 8)) * PITCH + (c % (R / 8)) * 8) = v[i];
-      }
+    for (int q = 0; q < NI; ++q) {
+      const bool ok = st.rok[q] && k0 + st.kofs[q] < kend;
+      const void* src = ok ? (const void*)(st.p[q] + kstep) : (const void*)g_zero16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(S + (wave + NW * q) * 512),
+                                       16, 0, 0);
     }
   }
 
@@ -389,14 +403,15 @@ struct BigOperand {
     } else {
       const int j = lane & 15;
       const int col = row0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-      const bf16* p = S + (ks * 16 + 8 * h2 + (j >> 2)) * PITCH + col;
+      const int kr = ks * 16 + 8 * h2 + (j >> 2);
+      const bf16* p0 = S + kr * R + (mphys(kr, col >> 3) << 3) + (col & 7);
+      const bf16* p1 = S + (kr + 4) * R + (mphys(kr + 4, col >> 3) << 3) + (col & 7);
       union {
         v4i16 s[2];
         bf16x8_t v;
       } r;
-      r.s[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
-      r.s[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4i16*)(p + 4 * PITCH));
+      r.s[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+      r.s[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
       return r.v;
     }
   }
@@ -423,16 +438,22 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, i
   tn = r / gsize;
 }
 
+// Waves per workgroup: 8 (4 x 2, wave tiles of 64 x BN/2).  (Four waves of
+// 128 x 128 were measured no faster at 256 x 256.)
+template <int BN> struct BigWaves { static constexpr int NW = 8; };
+
 template <int BM, int BN, bool AKM, bool BKM>
 struct BigSmem {
-  using OA = BigOperand<BM, AKM>;
-  using OB = BigOperand<BN, BKM>;
+  static constexpr int NW = BigWaves<BN>::NW;
+  using OA = BigOperand<BM, AKM, NW>;
+  using OB = BigOperand<BN, BKM, NW>;
   static constexpr int STAGE = OA::ELEMS + OB::ELEMS;
-  static constexpr int ELEMS = 2 * STAGE;
 };
 
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int BM, int BN, bool AKM, bool BKM, int MODE>
-__global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int K,
+__global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, int N, int K,
                                                                const bf16* __restrict__ A, int64_t lda,
                                                                const bf16* __restrict__ B, int64_t ldb,
                                                                Epilogue e, int kps, int tiles_m,
@@ -440,8 +461,12 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
   using SM = BigSmem<BM, BN, AKM, BKM>;
   using OA = typename SM::OA;
   using OB = typename SM::OB;
-  __shared__ __attribute__((aligned(16))) bf16 smem[SM::ELEMS];
-  constexpr int WM = BM / 4, WN = BN / 2, TI = WM / 32, TJ = WN / 32;
+  // Two stages as two separate arrays, so that the compiler can see that
+  // the loads streaming into one never alias the fragment reads of the other.
+  __shared__ __attribute__((aligned(16))) bf16 smem0[SM::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 smem1[SM::STAGE];
+  constexpr int NW = SM::NW;
+  constexpr int WM = BM / (NW / 2), WN = BN / 2, TI = WM / 32, TJ = WN / 32;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
   const int wm = wave / 2, wn = wave % 2;
   int tm, tn;
@@ -459,36 +484,17 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // NST register stages: tile t lives in stage t % NST from its global load
-  // (issued NST k-tiles ahead of its use) until its LDS store.  Tiles up to
-  // 256 x 192 afford two stages within 256 registers per lane; 256 x 256 one.
-  constexpr int NST = BN == 256 ? 1 : 2;
-  OA sa[NST];
-  OB sb[NST];
-  auto As = [&](int buf) { return smem + buf * SM::STAGE; };
-  auto Bs = [&](int buf) { return smem + buf * SM::STAGE + OA::ELEMS; };
-
-  if (nk > 0) {
-    sa[0].load(A, lda, m0, M, kbeg, kend);
-    sb[0].load(B, ldb, n0, N, kbeg, kend);
-    if constexpr (NST == 2) {
-      if (nk > 1) {
-        sa[NST - 1].load(A, lda, m0, M, kbeg + 64, kend);
-        sb[NST - 1].load(B, ldb, n0, N, kbeg + 64, kend);
-      }
-    }
-    sa[0].store(As(0));
-    sb[0].store(Bs(0));
-    if (nk > NST) {
-      sa[0].load(A, lda, m0, M, kbeg + NST * 64, kend);
-      sb[0].load(B, ldb, n0, N, kbeg + NST * 64, kend);
-    }
-  }
-  __syncthreads();
-
-  auto mma_tile = [&](int buf) {
-    const bf16* a_s = As(buf);
-    const bf16* b_s = Bs(buf);
+  typename OA::Src srcA;
+  typename OB::Src srcB;
+  OA::init(srcA, A, lda, m0, M, wave, lane);
+  OB::init(srcB, B, ldb, n0, N, wave, lane);
+  auto issue = [&](bf16* st, int k0) {
+    OA::load(st, srcA, lda, k0, kend, wave, lane);
+    OB::load(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
+  };
+  auto mma_tile = [&](const bf16* st) {
+    const bf16* a_s = st;
+    const bf16* b_s = st + OA::ELEMS;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t a[TI];
@@ -503,48 +509,49 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
       }
     }
   };
-  // iteration kt: store tile kt+1 (register stage (kt+1) % NST) to LDS buffer
-  // (kt+1) % 2, refill that register stage with tile kt+1+NST, multiply tile kt.
-  auto step = [&](int kt, auto lb_c) {
-    constexpr int lb = decltype(lb_c)::value;  // == (kt + 1) % 2
-    constexpr int st = lb % NST;
-    if (kt + 1 < nk) {
-      sa[st].store(As(lb));
-      sb[st].store(Bs(lb));
-      if (kt + 1 + NST < nk) {
-        sa[st].load(A, lda, m0, M, kbeg + (kt + 1 + NST) * 64, kend);
-        sb[st].load(B, ldb, n0, N, kbeg + (kt + 1 + NST) * 64, kend);
-      }
-    }
-    mma_tile(lb ^ 1);
+  // iteration kt multiplies the tile in `cur` while the next tile streams
+  // into `nxt`; one barrier per k-tile.
+  auto iter = [&](int kt, bf16* cur, bf16* nxt) {
+    if (kt + 1 < nk) issue(nxt, kbeg + (kt + 1) * 64);
+    // keep the loads at the top: the scheduler would otherwise sink them
+    // below the math, next to the wait that ends the iteration
+    __builtin_amdgcn_sched_barrier(0);
+    mma_tile(cur);
+    wait_vmem();
     __syncthreads();
   };
+
+  if (nk > 0) issue(smem0, kbeg);
+  wait_vmem();
+  __syncthreads();
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    step(kt, std::integral_constant<int, 1>());
-    step(kt + 1, std::integral_constant<int, 0>());
+    iter(kt, smem0, smem1);
+    iter(kt + 1, smem1, smem0);
   }
-  if (kt < nk) step(kt, std::integral_constant<int, 1>());
+  if (kt < nk) iter(kt, smem0, smem1);
 
-  // Epilogue through LDS: each wave stages 16 rows x WN of fp32 at a time
+  // Epilogue through LDS: each wave stages SLAB rows x WN of fp32 at a time
   // (the accumulator layout spreads a row over 32 lanes) and reads them back
   // as 8 consecutive columns per lane for 16-byte global accesses.
   constexpr int SP = WN + 4;
-  static_assert(8 * 16 * SP * 4 <= SM::ELEMS * 2, "epilogue staging exceeds LDS");
-  float* stage = reinterpret_cast<float*>(smem) + wave * 16 * SP;
+  constexpr int SLAB = NW * 16 * SP * 4 <= SM::STAGE * 2 ? 16 : 8;  // rows per round
+  constexpr int RPR = SLAB / 2;  // accumulator registers per round (8 rows per 4 registers)
+  static_assert(NW * SLAB * SP * 4 <= SM::STAGE * 2, "epilogue staging exceeds LDS");
+  float* stage = reinterpret_cast<float*>(smem0) + wave * SLAB * SP;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int part = 0; part < 16 / RPR; ++part) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const int r = 8 * half + rr;
+        for (int rr = 0; rr < RPR; ++rr) {
+          const int r = RPR * part + rr;
           stage[(8 * (rr / 4) + 4 * h2 + (rr % 4)) * SP + j * 32 + l32] = acc[i][j][r];
         }
       __syncthreads();
-      constexpr int CHUNKS = 16 * WN / 8;  // 8-column chunks in the slab
+      constexpr int CHUNKS = SLAB * WN / 8;  // 8-column chunks in the slab
 #pragma unroll
       for (int q = 0; q < (CHUNKS + 63) / 64; ++q) {
         const int c = lane + 64 * q;
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(BIG_THREADS) void gemm_big_kernel(int M, int N, int
           const float4 a = *reinterpret_cast<const float4*>(stage + row * SP + col);
           const float4 b = *reinterpret_cast<const float4*>(stage + row * SP + col + 4);
           const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          const int m = m0 + wm * WM + i * 32 + 16 * half + row, n = n0 + wn * WN + col;
+          const int m = m0 + wm * WM + i * 32 + SLAB * part + row, n = n0 + wn * WN + col;
           if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
         }
       }
@@ -595,7 +602,7 @@ struct Plan {
 constexpr bool big_square_ok(int mode) { return mode != EPI_BIAS_GELU && mode != EPI_GELU_BWD; }
 
 Plan plan_gemm(int M, int N, int K, int mode) {
-  if (M < 256 || N < 128) return {0, 1};
+  if (M < 256 || N < 128 || K % 8 != 0) return {0, 1};
   // kind: 1 = 256 x 256, 2 = 256 x 128, 3 = 256 x 192
   const int cand[3][3] = {{1, 256, 256}, {3, 256, 192}, {2, 256, 128}};
   const double eff[4] = {0.0, 1.0, 0.8, 0.92};
@@ -629,7 +636,7 @@ hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, in
   int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   int kps = (int)round_up(cdiv(K, splits), 64);
   dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
-#define GO(AK, BK_) gemm_big_kernel<BM, BN, AK, BK_, MODE><<<grid, BIG_THREADS, 0, s>>>(M, N, K, a, lda, b, ldb, e, kps, tiles_m, tiles_n)
+#define GO(AK, BK_) gemm_big_kernel<BM, BN, AK, BK_, MODE><<<grid, BigWaves<BN>::NW * 64, 0, s>>>(M, N, K, a, lda, b, ldb, e, kps, tiles_m, tiles_n)
   if (akm && bkm) GO(true, true);
   else if (akm && !bkm) GO(true, false);
   else if (!akm && !bkm) GO(false, false);
