@@ -25,6 +25,14 @@ METRIC = "train tokens/sec + MFU, GPT-2 124M bf16 B×T=16×1024, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 
+# HBM traffic of one lm_head forward GEMM launch from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), scaled by what the same
+# counters read for a plain 1 GiB device copy (FETCH_SIZE reads half the
+# bytes copied: factor 2.0; WRITE_SIZE is exact: factor 1.0).  Valid only for
+# the GEMM source it was measured on (first 16 hex digits of its sha256).
+LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "2c5e6b5464da1405", "fetch_kib": 916336, "write_kib": 1609728,
+                   "fetch_factor": 2.0, "write_factor": 1.0}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -45,18 +53,21 @@ def parse():
 
 
 def time_kernel(fn, stream, iters=20):
-    """Average duration (s) of fn() launches, HIP events on `stream`."""
+    """Average duration (s) of one fn() launch: a HIP event pair around each
+    launch on `stream`, so gaps between launches are not counted."""
     import torch
     with torch.cuda.stream(stream):
         fn()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
+        pairs = []
         for _ in range(iters):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
             fn()
-        end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / 1e3 / iters
+            b.record(stream)
+            pairs.append((a, b))
+    stream.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / 1e3 / iters
 
 
 def roofline_lm_head(cfg, stream):
@@ -74,10 +85,18 @@ def roofline_lm_head(cfg, stream):
                                    stream=stream), stream)
     flops = 2.0 * M * N * K
     achieved = flops / t / 1e12
+    traffic = None
+    import hashlib
+    src = os.path.join(ROOT, "transformer_lm_pretraining_train_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    tr = LM_HEAD_TRAFFIC
+    if sha == tr["gemm_source_sha256_16"] and (M, N, K) == (16384, 50304, 768):
+        traffic = int(tr["fetch_kib"] * 1024 * tr["fetch_factor"] + tr["write_kib"] * 1024 * tr["write_factor"])
     return {"kernel": "gemm_big_kernel<256,256,true,true,EPI_STORE> (lm_head forward, "
                       f"M={M} N={N} K={K})",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "traffic_unit": "bytes per launch", "algorithmic_bytes": 2 * (M * K + N * K + M * N),
             "avg_launch_us": round(t * 1e6, 1)}
 
 
