@@ -4,7 +4,9 @@ A step is zero_grad, k micro-steps of forward + backward (B x T tokens each,
 inputs already resident in HBM), then global-norm clip + AdamW.  Prints one
 JSON line with whole-job tokens/s, ms/step, MFU (6 N + 6 L T C flops per
 token against the bf16 dense MFMA peak), a roofline entry for the dominant
-kernel (timed with HIP events on the stream it runs on) and the CPU oracle's
+kernel (every launch of it inside the timed steps bracketed by HIP event
+pairs on the library's stream), the same figures for the other main kernels
+(from one extra step each, outside the timed region) and the CPU oracle's
 throughput on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_124m]
@@ -52,41 +54,16 @@ def parse():
     return ap.parse_args()
 
 
-def time_kernel(fn, stream, iters=20):
-    """Average duration (s) of one fn() launch: a HIP event pair around each
-    launch on `stream`, so gaps between launches are not counted."""
-    import torch
-    with torch.cuda.stream(stream):
-        fn()
-        pairs = []
-        for _ in range(iters):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            pairs.append((a, b))
-    stream.synchronize()
-    return sum(a.elapsed_time(b) for a, b in pairs) / 1e3 / iters
-
-
-def roofline_lm_head(cfg, stream):
+def lm_head_roofline(cfg, n, total_ms):
     """bf16 lm_head forward GEMM (M = B*T, N = Vp, K = C): the largest single
-    launch of the step.  Algorithmic flops per launch 2 M N K."""
-    import torch
-    import transformer_lm_pretraining_train_amd as g
-    M, N, K = cfg.micro_batch * cfg.seq_len, cfg.padded_vocab_size, cfg.n_embd
-    ldl = ((N + 63) // 64) * 64
-    with torch.cuda.stream(stream):
-        A = torch.randn((M, K), device="cuda").to(torch.bfloat16)
-        B = torch.randn((N, K), device="cuda").to(torch.bfloat16)
-        out = torch.empty((M, ldl), dtype=torch.bfloat16, device="cuda")
-    t = time_kernel(lambda: g.gemm(g.GPT2_BF16, True, True, M, N, K, A, K, B, K, "store", out, ldl,
-                                   stream=stream), stream)
-    flops = 2.0 * M * N * K
-    achieved = flops / t / 1e12
-    traffic = None
+    launch of the step, one per micro-step.  Algorithmic flops per launch
+    2 M N K; duration from the library's event pairs around each launch of it
+    inside the timed steps."""
     import hashlib
+    M, N, K = cfg.micro_batch * cfg.seq_len, cfg.padded_vocab_size, cfg.n_embd
+    t = total_ms / 1e3 / n
+    achieved = 2.0 * M * N * K / t / 1e12
+    traffic = None
     src = os.path.join(ROOT, "transformer_lm_pretraining_train_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     tr = LM_HEAD_TRAFFIC
@@ -97,7 +74,36 @@ def roofline_lm_head(cfg, stream):
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "traffic_unit": "bytes per launch", "algorithmic_bytes": 2 * (M * K + N * K + M * N),
-            "avg_launch_us": round(t * 1e6, 1)}
+            "avg_launch_us": round(t * 1e6, 1), "launches_timed": n}
+
+
+def other_kernels(cfg, n_timed):
+    """Algorithmic work per launch of the other timed steps: causal attention
+    (4 hd flops per query-key pair forward, 10 hd backward), the fused
+    cross-entropy forward (one bf16 read of each logit row) and AdamW (30
+    bytes per parameter: read p, g, m, v, write p, m, v and the bf16 copy)."""
+    import transformer_lm_pretraining_train_amd as g
+    B, T, H, C = cfg.micro_batch, cfg.seq_len, cfg.n_head, cfg.n_embd
+    hd = C // H
+    pairs = B * H * T * (T + 1) // 2
+    work = {"attn_fwd": (4.0 * hd * pairs, "mfma"), "attn_bwd": (10.0 * hd * pairs, "mfma"),
+            "ce_fwd": (2.0 * B * T * cfg.padded_vocab_size, "hbm"),
+            "adamw": (30.0 * g.num_params(cfg), "hbm")}
+    out = {}
+    for name, (n, ms) in n_timed.items():
+        w, bound = work[name]
+        t = ms / 1e3 / n
+        if bound == "mfma":
+            a = w / t / 1e12
+            out[name] = {"bound": bound, "achieved": round(a, 2), "unit": "TFLOP/s",
+                         "peak": PEAK_BF16_TFLOPS, "frac": round(a / PEAK_BF16_TFLOPS, 4),
+                         "avg_launch_us": round(t * 1e6, 1), "launches_timed": n}
+        else:
+            a = w / t / 1e9
+            out[name] = {"bound": bound, "achieved": round(a, 1), "unit": "GB/s",
+                         "peak": PEAK_HBM_GBS, "frac": round(a / PEAK_HBM_GBS, 4),
+                         "avg_launch_us": round(t * 1e6, 1), "launches_timed": n}
+    return out
 
 
 def cpu_baseline(wl, B_sample):
@@ -176,6 +182,8 @@ def main():
             step(s + 1)
             log(f"warmup step {s + 1}: loss {losses.mean().item():.4f} norm {norm.item():.4f}")
         stream.synchronize()
+        if not args.no_roofline:
+            model.set_kernel_timer("lm_head_fwd", args.steps * wl.grad_accum)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -193,10 +201,20 @@ def main():
     fpt = g.flops_per_token(cfg)
     mfu = fpt * tps / (PEAK_BF16_TFLOPS * 1e12)
 
-    roof = None
+    roof = others = None
     if not args.no_roofline:
-        roof = roofline_lm_head(cfg, stream)
+        roof = lm_head_roofline(cfg, *model.read_kernel_timer())
         log(f"roofline: {roof}")
+        # one more step per timed kernel, outside the timed region
+        timed = {}
+        with torch.cuda.stream(stream):
+            for s, name in enumerate(("attn_fwd", "attn_bwd", "ce_fwd", "adamw")):
+                model.set_kernel_timer(name, 4096)
+                step(args.warmup + args.steps + s + 1)
+                timed[name] = model.read_kernel_timer()
+            model.set_kernel_timer("none")
+        others = other_kernels(cfg, timed)
+        log(f"other kernels: {others}")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -213,7 +231,7 @@ def main():
                    "seq_len": wl.seq_len, "grad_accum": wl.grad_accum,
                    "tokens_per_step": wl.tokens_per_step, "parallelism": "single-gpu"},
         "mfu": round(mfu, 4), "flops_per_token": fpt,
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "other_kernels": others, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -172,6 +172,33 @@ enum {
 };
 int gpt2_debug_read(gpt2_model* model, int which, int layer, void* dev_dst, size_t bytes);
 
+/* Measurement hook: when set, the library records a HIP event pair on its
+ * stream around every launch of the chosen step, for up to max_launches
+ * launches (further launches run untimed).  The events are created here
+ * (host-side objects; no device memory is allocated), so set the timer
+ * outside a timed region.  which = GPT2_TIMER_NONE releases the events.
+ * Waits for the stream first.  EINVAL on an unknown `which` or
+ * max_launches outside [1, 2^20]; EHIP if event creation fails.
+ *   LM_HEAD_FWD  the tied-head logits GEMM of each forward
+ *   ATTN_FWD     causal attention forward, one pair per layer
+ *   ATTN_BWD     attention backward (both of its kernels), one pair per layer
+ *   CE_FWD       the fused softmax cross-entropy forward of each forward
+ *   ADAMW        the AdamW update of each optimizer step (not the norm) */
+enum {
+  GPT2_TIMER_NONE = 0,
+  GPT2_TIMER_LM_HEAD_FWD = 1,
+  GPT2_TIMER_ATTN_FWD = 2,
+  GPT2_TIMER_ATTN_BWD = 3,
+  GPT2_TIMER_CE_FWD = 4,
+  GPT2_TIMER_ADAMW = 5
+};
+int gpt2_set_kernel_timer(gpt2_model* model, int which, int max_launches);
+
+/* Waits for the stream, then reports how many launches were timed since the
+ * timer was set or last read (*launches) and the sum of their event-pair
+ * durations in milliseconds (*total_ms), and restarts the count. */
+int gpt2_read_kernel_timer(gpt2_model* model, int* launches, double* total_ms);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* gpt2_last_error(void);
 

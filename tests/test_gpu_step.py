@@ -267,3 +267,26 @@ def test_zero_lr_leaves_params_and_clip_below_threshold():
     mm, vv, step = m.get_opt_state()
     # below the clip threshold the gradient is used unscaled: m = 0.1 g exactly-ish
     assert rel_l2(host(mm), 0.1 * gv) < 1e-6
+
+
+def test_kernel_timer_counts_launches_and_leaves_results_unchanged():
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "fp32", k=2)
+    _, ref = gpu_step(cfg, flat, batches)
+    m = g.Model(cfg)
+    m.set_params(to_dev(flat))
+    with pytest.raises(g.GPT2Error) as ei:
+        m.set_kernel_timer("lm_head_fwd", 0)
+    assert ei.value.name == "EINVAL"
+    m.set_kernel_timer("attn_fwd", 5)  # 2 micro-steps x 4 layers = 8 launches, 5 timed
+    _, out = gpu_step(cfg, flat, batches, model=m)
+    n, ms = m.read_kernel_timer()
+    assert n == 5 and ms > 0.0
+    assert m.read_kernel_timer() == (0, 0.0)
+    # the embedding backward adds with atomics, so only near-equality holds
+    assert rel_l2(out[0]["params"], ref[0]["params"]) < 1e-6
+    m.set_kernel_timer("lm_head_fwd", 16)
+    m.forward(to_dev(batches[0][0]), to_dev(batches[0][1]), None)
+    assert m.read_kernel_timer()[0] == 1
+    m.set_kernel_timer("none")
+    m.forward(to_dev(batches[0][0]), to_dev(batches[0][1]), None)
+    assert m.read_kernel_timer() == (0, 0.0)

@@ -29,6 +29,7 @@ ERRORS = {0: "OK", -1: "EINVAL", -2: "EWORKSPACE", -3: "ESTATE", -4: "ETOKEN",
 EPI = {"store": 0, "bias": 1, "bias_resid": 2, "bias_gelu": 3, "gelu_bwd": 4, "acc_f32": 5}
 DBG = {"logits": 0, "losses": 1, "argmax": 2, "ln1": 3, "qkv": 4, "atty": 5, "res2": 6,
        "fch": 7, "res3": 8, "lnf": 9, "att_lse": 10, "encoded": 11}
+TIMER = {"none": 0, "lm_head_fwd": 1, "attn_fwd": 2, "attn_bwd": 3, "ce_fwd": 4, "adamw": 5}
 
 
 class GPT2Config(ctypes.Structure):
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
             "gpt2_clip_and_adamw": (I, [P, F, F, F, F, F, F, P]),
             "gpt2_sync": (I, [P]),
             "gpt2_debug_read": (I, [P, I, I, P, SZ]),
+            "gpt2_set_kernel_timer": (I, [P, I, I]),
+            "gpt2_read_kernel_timer": (I, [P, ctypes.POINTER(I), ctypes.POINTER(ctypes.c_double)]),
             "gpt2_last_error": (ctypes.c_char_p, []),
             "gpt2k_gemm": (I, [I, I, I, I, I, I, P, I64, P, I64, I, P, I64, P, P, I64, P, I64, P,
                                I64, P, SZ, P]),
@@ -242,6 +245,17 @@ class Model:
 
     def sync(self):
         _check(lib().gpt2_sync(self.h))
+
+    def set_kernel_timer(self, name, max_launches=4096):
+        """Bracket every launch of one step (TIMER key) with a HIP event pair."""
+        _check(lib().gpt2_set_kernel_timer(self.h, TIMER[name], max_launches))
+
+    def read_kernel_timer(self):
+        """(launches timed since the last read, their summed duration in ms)."""
+        n = ctypes.c_int(0)
+        ms = ctypes.c_double(0.0)
+        _check(lib().gpt2_read_kernel_timer(self.h, ctypes.byref(n), ctypes.byref(ms)))
+        return n.value, ms.value
 
     def debug_read(self, name, out, layer=0):
         _check(lib().gpt2_debug_read(self.h, DBG[name], layer, _ptr(out),

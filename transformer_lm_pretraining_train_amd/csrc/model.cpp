@@ -164,6 +164,10 @@ struct gpt2_model {
   const int32_t* targets;
   bool have_targets;
   int64_t step;
+  // optional HIP event pairs around one kind of launch (gpt2_set_kernel_timer)
+  int timer_which = GPT2_TIMER_NONE;
+  int timer_cap = 0, timer_used = 0;
+  std::vector<hipEvent_t> timer_ev;
 
   // weights in the GEMM input type
   const void* wt(int64_t off) const {
@@ -258,6 +262,26 @@ int check_launch(hipError_t e, const char* what) {
     int rc_ = check_launch((expr), #expr);           \
     if (rc_ != GPT2_OK) return rc_;                  \
   } while (0)
+
+// Brackets one launch with a HIP event pair on the model's stream when the
+// timer is set to `which` and has events left.
+#define TIMED(which, expr)                                                          \
+  do {                                                                              \
+    const bool on_ = md->timer_which == (which) && md->timer_used < md->timer_cap;  \
+    if (on_) HIP_TRY(hipEventRecord(md->timer_ev[2 * md->timer_used], md->stream)); \
+    LAUNCH(expr);                                                                   \
+    if (on_) {                                                                      \
+      HIP_TRY(hipEventRecord(md->timer_ev[2 * md->timer_used + 1], md->stream));    \
+      ++md->timer_used;                                                             \
+    }                                                                               \
+  } while (0)
+
+void release_timer(gpt2_model* md) {
+  for (hipEvent_t e : md->timer_ev) (void)hipEventDestroy(e);
+  md->timer_ev.clear();
+  md->timer_which = GPT2_TIMER_NONE;
+  md->timer_cap = md->timer_used = 0;
+}
 
 Epilogue epi(int mode, void* out, int64_t ldo) {
   Epilogue e{};
@@ -379,6 +403,7 @@ int gpt2_create(const gpt2_config* cfg, void* dev_workspace, size_t bytes, void*
 }
 
 int gpt2_destroy(gpt2_model* md) {
+  if (md) release_timer(md);
   delete md;
   return GPT2_OK;
 }
@@ -453,7 +478,8 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     Epilogue e = epi(EPI_BIAS, a.qkv, 3 * C);
     e.bias = P + o.qkv_b;
     LAUNCH(gemm(dt, true, true, M, 3 * C, C, a.ln1, C, md->wt(o.qkv_w), C, e, s));
-    LAUNCH(attention_forward(dt, a.atty, a.lse, a.qkv, md->B, md->Tn, H, md->hd, s));
+    TIMED(GPT2_TIMER_ATTN_FWD,
+          attention_forward(dt, a.atty, a.lse, a.qkv, md->B, md->Tn, H, md->hd, s));
     e = epi(EPI_BIAS_RESID, a.res2, C);
     e.bias = P + o.proj_b;
     e.resid = x;
@@ -476,11 +502,12 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   LAUNCH(layernorm_forward(dt, md->lnf, md->lnf_mean, md->lnf_rstd, x, P + Ly.lnf_w, P + Ly.lnf_b,
                            M, C, eps, s));
   // logits over the padded vocabulary (tied head: wte)
-  LAUNCH(gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
-              epi(EPI_STORE, md->logits, md->ldl), s));
+  TIMED(GPT2_TIMER_LM_HEAD_FWD, gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
+                                     epi(EPI_STORE, md->logits, md->ldl), s));
   if (targets) {
-    LAUNCH(crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax, md->logits, md->ldl,
-                                targets, M, md->V, md->err_flag, s));
+    TIMED(GPT2_TIMER_CE_FWD, crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax,
+                                                  md->logits, md->ldl, targets, M, md->V,
+                                                  md->err_flag, s));
     LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
     md->have_targets = true;
   }
@@ -537,8 +564,8 @@ int gpt2_backward(gpt2_model* md) {
     LAUNCH(bias_grad(dt, G + o.proj_b, md->dres, M, C, C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, C, md->dres, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(attention_backward(dt, md->dqkv, md->dbuf_c, a.qkv, a.atty, a.lse, md->B, md->Tn, H,
-                              md->hd, md->scratch, s));
+    TIMED(GPT2_TIMER_ATTN_BWD, attention_backward(dt, md->dqkv, md->dbuf_c, a.qkv, a.atty, a.lse,
+                                                  md->B, md->Tn, H, md->hd, md->scratch, s));
     // qkv = ln1 qkv_w^T + qkv_b
     LAUNCH(gemm(dt, false, false, 3 * C, C, M, md->dqkv, 3 * C, a.ln1, C,
                 epi(EPI_ACC_F32, G + o.qkv_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
@@ -578,9 +605,10 @@ int gpt2_clip_and_adamw(gpt2_model* md, float lr, float beta1, float beta2, floa
   const int64_t t = md->step + 1;
   const float bc1 = (float)(1.0 - std::pow((double)beta1, (double)t));
   const float bc2 = (float)(1.0 - std::pow((double)beta2, (double)t));
-  LAUNCH(adamw(md->params, md->grads, md->m, md->v, md->dt == BF16 ? md->shadow : nullptr, md->N,
-               lr, beta1, beta2, eps, weight_decay, bc1, bc2, grad_norm_result(md->norm_scratch),
-               decay_map(md), s));
+  TIMED(GPT2_TIMER_ADAMW,
+        adamw(md->params, md->grads, md->m, md->v, md->dt == BF16 ? md->shadow : nullptr, md->N,
+              lr, beta1, beta2, eps, weight_decay, bc1, bc2, grad_norm_result(md->norm_scratch),
+              decay_map(md), s));
   float res[2] = {0.f, 0.f};
   HIP_TRY(hipMemcpyAsync(res, grad_norm_result(md->norm_scratch), sizeof(res),
                          hipMemcpyDeviceToHost, s));
@@ -589,6 +617,44 @@ int gpt2_clip_and_adamw(gpt2_model* md, float lr, float beta1, float beta2, floa
     return fail(GPT2_ENONFINITE, "gradient norm is %f: update skipped", (double)res[0]);
   md->step = t;
   return gpt2_sync(md);
+}
+
+int gpt2_set_kernel_timer(gpt2_model* md, int which, int max_launches) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (which < GPT2_TIMER_NONE || which > GPT2_TIMER_ADAMW)
+    return fail(GPT2_EINVAL, "unknown timer %d", which);
+  if (which != GPT2_TIMER_NONE && (max_launches < 1 || max_launches > (1 << 20)))
+    return fail(GPT2_EINVAL, "max_launches must be in [1, 2^20]");
+  HIP_TRY(hipStreamSynchronize(md->stream));
+  release_timer(md);
+  if (which == GPT2_TIMER_NONE) return GPT2_OK;
+  md->timer_ev.resize(2 * (size_t)max_launches);
+  for (size_t i = 0; i < md->timer_ev.size(); ++i) {
+    hipError_t e = hipEventCreate(&md->timer_ev[i]);
+    if (e != hipSuccess) {
+      md->timer_ev.resize(i);
+      release_timer(md);
+      return fail(GPT2_EHIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  md->timer_which = which;
+  md->timer_cap = max_launches;
+  return GPT2_OK;
+}
+
+int gpt2_read_kernel_timer(gpt2_model* md, int* launches, double* total_ms) {
+  if (!md || !launches || !total_ms) return fail(GPT2_EINVAL, "NULL argument");
+  HIP_TRY(hipStreamSynchronize(md->stream));
+  double sum = 0.0;
+  for (int i = 0; i < md->timer_used; ++i) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, md->timer_ev[2 * i], md->timer_ev[2 * i + 1]));
+    sum += ms;
+  }
+  *launches = md->timer_used;
+  *total_ms = sum;
+  md->timer_used = 0;
+  return GPT2_OK;
 }
 
 int gpt2_debug_read(gpt2_model* md, int which, int layer, void* dst, size_t bytes) {
