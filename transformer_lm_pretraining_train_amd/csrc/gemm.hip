@@ -328,13 +328,21 @@ constexpr int BIG_THREADS = 512;  // 8 waves: 4 along M x 2 along N
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-// Source of the zero vectors that out-of-range operand loads read.
-__device__ __attribute__((aligned(16))) uint4 g_zero16[1] = {{0u, 0u, 0u, 0u}};
+// Buffer-resource word 3 for raw (unswizzled, stride 0) buffers on CDNA:
+// 32-bit data format, range checking against num_records.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+// A per-lane buffer offset that is always out of range: the load returns
+// zeros (and writes them to LDS) without touching memory.
+constexpr uint32_t kOOB = 0x80000000u;
 
 // One operand tile (R rows of the output dimension x 64 k) in LDS, filled
-// by direct global->LDS loads: one wave instruction writes 64 consecutive
-// 16-byte slots, lane i at slot i, and each lane fetches the global vector
-// that belongs in its slot.  No registers hold the tile in flight.
+// by buffer loads straight into LDS: one wave instruction writes 64
+// consecutive 16-byte slots, lane i at slot i, and each lane fetches the
+// global vector that belongs in its slot.  No registers hold the tile in
+// flight.  Each lane's byte offset inside the operand is fixed for the whole
+// k loop; the k step goes into the scalar offset, and rows past the matrix
+// edge carry an out-of-range offset, so the hardware range check supplies
+// their zeros.
 //  k-major source: [row][64 k], 128-byte rows, 16-byte chunks XOR-swizzled
 //    by row (conflict-free 16-byte fragment reads).
 //  m-major source: [64 k][R rows] as in memory, the chunks of k-row k
@@ -350,48 +358,52 @@ struct BigOperand {
   __device__ __forceinline__ static int mphys(int krow, int lc) { return (lc + CPR - 4 * (krow & 3)) % CPR; }
   __device__ __forceinline__ static int mlog(int krow, int p) { return (p + 4 * (krow & 3)) % CPR; }
 
-  // Per-lane source of each of the NI load instructions, fixed for the whole
-  // k loop: the vector at k-offset kofs[q] (relative to a tile's first k)
-  // of a row that is in range (rok) or not.
   struct Src {
-    const bf16* p[NI];
-    int kofs[NI];
-    bool rok[NI];
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t voff[NI];  // byte offset of each load's vector for k0 = 0, or kOOB
+    int kofs[NI];       // its k offset inside a tile (masks a ragged last tile)
   };
 
+  // P: the operand, ld: its row pitch in elements, row0: first output row of
+  // this tile, rows_total: rows of the output dimension, K: the k extent.
+  // The host guarantees that the operand spans fewer than 2^31 bytes.
   __device__ __forceinline__ static void init(Src& st, const bf16* __restrict__ P, int64_t ld,
-                                              int row0, int rows_total, int wave, int lane) {
+                                              int row0, int rows_total, int K, int wave, int lane) {
+    const bf16* base = KMAJOR ? P + (int64_t)row0 * ld : P + row0;
+    const int64_t span = KMAJOR ? ((int64_t)(rows_total - 1 - row0) * ld + K) * 2
+                                : ((int64_t)(K - 1) * ld + (rows_total - row0)) * 2;
+    st.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)span, (int)kRsrcWord3);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
       const int slot = (wave + NW * q) * 64 + lane;
-      int gr, ko;
       if constexpr (KMAJOR) {
         const int row = slot >> 3;
-        gr = row0 + row;
-        ko = 8 * ((slot & 7) ^ swz(row));
-        st.p[q] = P + (int64_t)gr * ld + ko;
+        const int ko = 8 * ((slot & 7) ^ swz(row));
+        st.voff[q] = row0 + row < rows_total ? (uint32_t)(((int64_t)row * ld + ko) * 2) : kOOB;
+        st.kofs[q] = ko;
       } else {
         const int krow = slot / CPR;
-        gr = row0 + 8 * mlog(krow, slot % CPR);
-        ko = krow;
-        st.p[q] = P + (int64_t)krow * ld + gr;
+        const int c = 8 * mlog(krow, slot % CPR);
+        st.voff[q] = row0 + c < rows_total ? (uint32_t)(((int64_t)krow * ld + c) * 2) : kOOB;
+        st.kofs[q] = krow;
       }
-      st.kofs[q] = ko;
-      st.rok[q] = gr < rows_total;
     }
   }
 
-  // Issue the direct loads of the tile starting at k0 into LDS tile S.
+  // Issue the loads of the tile starting at k0 into LDS tile S.  TAIL: this
+  // tile extends past kend, whose columns (k-major) or rows (m-major) must
+  // read as zeros.
+  template <bool TAIL>
   __device__ __forceinline__ static void load(bf16* __restrict__ S, const Src& st, int64_t ld,
-                                              int k0, int kend, int wave, int lane) {
-    const int64_t kstep = KMAJOR ? (int64_t)k0 : (int64_t)k0 * ld;
+                                              int k0, int kend, int wave) {
+    const uint32_t soff = (uint32_t)(KMAJOR ? (int64_t)k0 * 2 : (int64_t)k0 * ld * 2);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const bool ok = st.rok[q] && k0 + st.kofs[q] < kend;
-      const void* src = ok ? (const void*)(st.p[q] + kstep) : (const void*)g_zero16;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(S + (wave + NW * q) * 512),
-                                       16, 0, 0);
+      const uint32_t v = TAIL && k0 + st.kofs[q] >= kend ? kOOB : st.voff[q];
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist only for the GPU target
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          st.rs, (__attribute__((address_space(3))) void*)(S + (wave + NW * q) * 512), 16, v, soff, 0, 0);
+#endif
     }
   }
 
@@ -415,7 +427,21 @@ struct BigOperand {
       return r.v;
     }
   }
+  // LDS read instructions per fragment
+  static constexpr int READS = KMAJOR ? 1 : 2;
 };
+
+// Scheduling hint for one k-step of NM MFMAs while the NR LDS reads of the
+// next k-step are issued: the reads are spread evenly between the MFMAs.
+template <int NM, int NR, int I = 0>
+__device__ __forceinline__ void interleave_mfma_reads() {
+  if constexpr (I < NM) {
+    constexpr int r = (I + 1) * NR / NM - I * NR / NM;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // r LDS reads
+    interleave_mfma_reads<NM, NR, I + 1>();
+  }
+}
 
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
                                             int& tn) {
@@ -467,7 +493,8 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
   __shared__ __attribute__((aligned(16))) bf16 smem1[SM::STAGE];
   constexpr int NW = SM::NW;
   constexpr int WM = BM / (NW / 2), WN = BN / 2, TI = WM / 32, TJ = WN / 32;
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
+  const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: LDS bases in SGPRs
   const int wm = wave / 2, wn = wave % 2;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
@@ -486,28 +513,32 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
 
   typename OA::Src srcA;
   typename OB::Src srcB;
-  OA::init(srcA, A, lda, m0, M, wave, lane);
-  OB::init(srcB, B, ldb, n0, N, wave, lane);
+  OA::init(srcA, A, lda, m0, M, K, wave, lane);
+  OB::init(srcB, B, ldb, n0, N, K, wave, lane);
   auto issue = [&](bf16* st, int k0) {
-    OA::load(st, srcA, lda, k0, kend, wave, lane);
-    OB::load(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
-  };
-  auto mma_tile = [&](const bf16* st) {
-    const bf16* a_s = st;
-    const bf16* b_s = st + OA::ELEMS;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t a[TI];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) a[i] = OA::frag(a_s, wm * WM + i * 32, s, lane);
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const bf16x8_t b = OB::frag(b_s, wn * WN + j * 32, s, lane);
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][j], 0, 0, 0);
-      }
+    if (k0 + 64 > kend) {
+      OA::template load<true>(st, srcA, lda, k0, kend, wave);
+      OB::template load<true>(st + OA::ELEMS, srcB, ldb, k0, kend, wave);
+    } else {
+      OA::template load<false>(st, srcA, lda, k0, kend, wave);
+      OB::template load<false>(st + OA::ELEMS, srcB, ldb, k0, kend, wave);
     }
+  };
+  // Fragments are double-buffered in registers: the LDS reads of k-step s+1
+  // are issued between the MFMAs of k-step s.
+  constexpr int NR = TI * OA::READS + TJ * OB::READS;  // LDS reads per k-step
+  auto frags = [&](const bf16* st, int s, bf16x8_t (&fa)[TI], bf16x8_t (&fb)[TJ]) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa[i] = OA::frag(st, wm * WM + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb[j] = OB::frag(st + OA::ELEMS, wn * WN + j * 32, s, lane);
+  };
+  auto mma = [&](const bf16x8_t (&fa)[TI], const bf16x8_t (&fb)[TJ]) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
   // iteration kt multiplies the tile in `cur` while the next tile streams
   // into `nxt`; one barrier per k-tile.
@@ -516,7 +547,22 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
     // keep the loads at the top: the scheduler would otherwise sink them
     // below the math, next to the wait that ends the iteration
     __builtin_amdgcn_sched_barrier(0);
-    mma_tile(cur);
+    bf16x8_t fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+    frags(cur, 0, fa0, fb0);
+    frags(cur, 1, fa1, fb1);
+    mma(fa0, fb0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);  // all reads of k-steps 0 and 1
+    __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);  // then the MFMAs of k-step 0
+    __builtin_amdgcn_sched_barrier(0);
+    frags(cur, 2, fa0, fb0);
+    mma(fa1, fb1);
+    interleave_mfma_reads<TI * TJ, NR>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(cur, 3, fa1, fb1);
+    mma(fa0, fb0);
+    interleave_mfma_reads<TI * TJ, NR>();
+    __builtin_amdgcn_sched_barrier(0);
+    mma(fa1, fb1);
     wait_vmem();
     __syncthreads();
   };
@@ -630,6 +676,11 @@ Plan plan_gemm(int M, int N, int K, int mode) {
   return best;
 }
 
+// Bytes an operand spans: rows x pitch (k-major) or K x pitch (m-major).
+int64_t operand_span(bool kmajor, int rows, int K, int64_t ld) {
+  return (kmajor ? (int64_t)rows : (int64_t)K) * ld * 2;
+}
+
 template <int BM, int BN, int MODE>
 hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, int64_t lda,
                       const bf16* b, int64_t ldb, const Epilogue& e, int splits, hipStream_t s) {
@@ -658,6 +709,10 @@ hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const vo
   const bf16* a = (const bf16*)A;
   const bf16* b = (const bf16*)B;
   Plan p = plan_gemm(M, N, K, MODE);
+  // the large-tile kernels address each operand through a buffer resource
+  // with 32-bit byte offsets
+  const int64_t span_a = (operand_span(akm, M, K, lda)), span_b = operand_span(bkm, N, K, ldb);
+  if (span_a >= (int64_t(1) << 31) || span_b >= (int64_t(1) << 31)) p = {0, 1};
   if (p.kind == 0) {
     dim3 grid((unsigned)cdiv(N, MF_BN), (unsigned)cdiv(M, MF_BM));
     if (akm && bkm) gemm_mfma_kernel<true, true, MODE><<<grid, 256, 0, s>>>(M, N, K, a, lda, b, ldb, e);
