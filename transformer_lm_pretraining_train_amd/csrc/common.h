@@ -56,23 +56,27 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // exp(x) via the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
-// tanh(u) = 1 - 2 / (exp(2u) + 1); saturates correctly at +-inf.
+// tanh(u) = 1 - 2 / (exp(2u) + 1); saturates correctly at +-inf.  The
+// hardware reciprocal (1 ulp) replaces the IEEE divide.
 __device__ __forceinline__ float tanh_from_exp(float u) {
   float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // exp(2u)
-  return 1.0f - 2.0f / (e + 1.0f);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
-// GELU, tanh form: 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))).
-__device__ __forceinline__ float gelu_f(float h) {
-  const float k = 0.7978845608028654f;
-  float t = tanh_from_exp(k * (h + 0.044715f * h * h * h));
-  return 0.5f * h * (1.0f + t);
+// GELU, tanh form: 0.5 h (1 + tanh(u)), u = sqrt(2/pi) (h + 0.044715 h^3).
+// With s = 1 / (1 + exp(-2u)) = (1 + tanh(u)) / 2 this is h s.
+__device__ __forceinline__ float gelu_sigmoid(float h) {
+  const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float u2 = k2 * h * __builtin_fmaf(0.044715f * h, h, 1.0f);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u2));
 }
-// d gelu / d h for the tanh form.
+__device__ __forceinline__ float gelu_f(float h) { return h * gelu_sigmoid(h); }
+// d gelu / d h = 0.5 (1 + t) + 0.5 h (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 h^2)
+//             = s + 2 h s (1 - s) sqrt(2/pi) (1 + 0.134145 h^2).
 __device__ __forceinline__ float gelu_grad_f(float h) {
-  const float k = 0.7978845608028654f;
-  float t = tanh_from_exp(k * (h + 0.044715f * h * h * h));
-  return 0.5f * (1.0f + t) + 0.5f * h * (1.0f - t * t) * k * (1.0f + 3.0f * 0.044715f * h * h);
+  const float s = gelu_sigmoid(h);
+  const float k = 2.0f * 0.7978845608028654f;
+  return __builtin_fmaf(k * h * s * (1.0f - s), __builtin_fmaf(3.0f * 0.044715f * h, h, 1.0f), s);
 }
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -533,12 +533,16 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) fb[j] = OB::frag(st + OA::ELEMS, wn * WN + j * 32, s, lane);
   };
+  // The B fragment goes in as the MFMA's first operand, so the accumulator
+  // holds the tile transposed: lane l has row l%32 of block i and, in
+  // registers 4q..4q+3, the four consecutive columns 8q + 4(l/32) + 0..3 of
+  // block j.
   auto mma = [&](const bf16x8_t (&fa)[TI], const bf16x8_t (&fb)[TJ]) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
   // iteration kt multiplies the tile in `cur` while the next tile streams
   // into `nxt`; one barrier per k-tile.
@@ -577,40 +581,46 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
   }
   if (kt < nk) iter(kt, smem0, smem1);
 
-  // Epilogue through LDS: each wave stages SLAB rows x WN of fp32 at a time
-  // (the accumulator layout spreads a row over 32 lanes) and reads them back
-  // as 8 consecutive columns per lane for 16-byte global accesses.
-  constexpr int SP = WN + 4;
-  constexpr int SLAB = NW * 16 * SP * 4 <= SM::STAGE * 2 ? 16 : 8;  // rows per round
-  constexpr int RPR = SLAB / 2;  // accumulator registers per round (8 rows per 4 registers)
-  static_assert(NW * SLAB * SP * 4 <= SM::STAGE * 2, "epilogue staging exceeds LDS");
-  float* stage = reinterpret_cast<float*>(smem0) + wave * SLAB * SP;
+  // Epilogue through LDS, per wave: the wave's 32 rows of block i and JB
+  // column blocks at a time go to its own LDS slab (16-byte writes of four
+  // consecutive columns), then come back as 8 consecutive columns per lane
+  // for 16-byte global accesses.  One workgroup barrier first (the slabs
+  // reuse the operand stages); after it each wave touches only its own slab,
+  // and a wave's LDS accesses complete in issue order.
+  constexpr int JB = (TJ % 3 == 0) ? 3 : 2;  // column blocks per round
+  constexpr int SP = JB * 32 + 4;            // slab row pitch (floats)
+  static_assert(TJ % JB == 0, "column blocks must divide evenly");
+  // waves 0 .. NW/2-1 stage in the first operand buffer, the others in the second
+  static_assert((NW / 2) * 32 * SP * 4 <= SM::STAGE * 2, "epilogue staging exceeds LDS");
+  float* slab = reinterpret_cast<float*>(wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * 32 * SP;
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
-    for (int part = 0; part < 16 / RPR; ++part) {
+    for (int jr = 0; jr < TJ / JB; ++jr) {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+      for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
-        for (int rr = 0; rr < RPR; ++rr) {
-          const int r = RPR * part + rr;
-          stage[(8 * (rr / 4) + 4 * h2 + (rr % 4)) * SP + j * 32 + l32] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          const f32x16_t& c = acc[i][jr * JB + jj];
+          *reinterpret_cast<float4*>(slab + l32 * SP + jj * 32 + 8 * q + 4 * h2) =
+              make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
         }
-      __syncthreads();
-      constexpr int CHUNKS = SLAB * WN / 8;  // 8-column chunks in the slab
+      __builtin_amdgcn_wave_barrier();
+      constexpr int CPRW = JB * 4;        // 8-column chunks per slab row
+      constexpr int CHUNKS = 32 * CPRW;   // chunks in the slab
+      static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
 #pragma unroll
-      for (int q = 0; q < (CHUNKS + 63) / 64; ++q) {
-        const int c = lane + 64 * q;
-        if (c < CHUNKS) {
-          const int row = c / (WN / 8), col = (c % (WN / 8)) * 8;
-          const float4 a = *reinterpret_cast<const float4*>(stage + row * SP + col);
-          const float4 b = *reinterpret_cast<const float4*>(stage + row * SP + col + 4);
-          const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          const int m = m0 + wm * WM + i * 32 + SLAB * part + row, n = n0 + wn * WN + col;
-          if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
-        }
+      for (int t = 0; t < CHUNKS / 64; ++t) {
+        const int c = lane + 64 * t;
+        const int row = c / CPRW, col = (c % CPRW) * 8;
+        const float4 a = *reinterpret_cast<const float4*>(slab + row * SP + col);
+        const float4 b = *reinterpret_cast<const float4*>(slab + row * SP + col + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const int m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + jr * JB * 32 + col;
+        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
       }
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
