@@ -32,6 +32,8 @@
 // LDS is double-buffered (one barrier per tile) with the next tile's global
 // loads in flight during the current tile's math.  Workgroups of the causal
 // passes are issued longest-first.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -153,9 +155,17 @@ __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x
 }
 
 // --------------------------------------------------------------- forward
-__global__ __launch_bounds__(256) void attn_fwd_mfma(bf16* __restrict__ out, float* __restrict__ lse,
-                                                     const bf16* __restrict__ qkv, int T, int H,
-                                                     int nqb) {
+// Online softmax with a lazily moved reference: each query keeps a running
+// reference m (log2 units) and accumulates l = sum exp2(s c - m) and
+// O = sum exp2(s c - m) v.  m is raised only when a tile's maximum exceeds it
+// by more than 8, so the probabilities stay below 2^8 (no fp32 overflow) and
+// most tiles skip the rescaling of O; l and O always share the same m, so the
+// result O / l and the log-sum-exp m + log2 l are exact.
+constexpr float RESCALE_LOG2 = 8.0f;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_mfma(
+    bf16* __restrict__ out, float* __restrict__ lse, const bf16* __restrict__ qkv, int T, int H,
+    int nqb) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
   const int qb = nqb - 1 - blockIdx.x;
@@ -184,6 +194,56 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(bf16* __restrict__ out, flo
     tile_load(rv, vbase, ld, TB, T);
   }
   __syncthreads();
+  // One 64-key tile for this wave's 32 queries; MASK on the tiles that reach
+  // past the wave's first query.
+  auto tile = [&](const bf16* Ks, const bf16* Vs, int k0, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    f32x16_t s[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[t] = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s[t]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASK) {
+          if (k0 + t * 32 + acc_row(r, h2) > myq) s[t][r] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[t][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    // move the reference only when this tile exceeds it by more than 2^8
+    const bool move = mx > m + RESCALE_LOG2;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float mnew = move ? mx : m;
+      const float alpha = exp2_(m - mnew);
+      m = mnew;
+      l *= alpha;
+      o[0] *= alpha;
+      o[1] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_(__builtin_fmaf(s[t][r], c, -m));
+        s[t][r] = p;
+        ps += p;
+      }
+    l += ps;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8_t pb = pack_b(s[t], u);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+          o[dt] = mfma(frag_tr(Vs, dt * 32, t * 32 + 16 * u, lane), pb, o[dt]);
+      }
+  };
   for (int kb = 0; kb < nkb; ++kb) {
     const bf16* Ks = smem + (kb & 1) * 2 * TILE;
     const bf16* Vs = Ks + TILE;
@@ -198,48 +258,8 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(bf16* __restrict__ out, flo
     }
     const int k0 = kb * TB;
     if (k0 <= qw + 31 && qw < T) {
-      f32x16_t s[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) s[t] = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s[t]);
-      const bool diag = k0 + TB - 1 > qw;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[t][r] * c;
-          if (diag && k0 + t * 32 + acc_row(r, h2) > myq) x = -INFINITY;
-          s[t][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx);
-      const float alpha = exp2_(m - mnew);
-      m = mnew;
-      l *= alpha;
-      o[0] *= alpha;
-      o[1] *= alpha;
-      float ps = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = exp2_(s[t][r] - mnew);
-          s[t][r] = p;
-          ps += p;
-        }
-      l += ps;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pb = pack_b(s[t], u);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt)
-            o[dt] = mfma(frag_tr(Vs, dt * 32, t * 32 + 16 * u, lane), pb, o[dt]);
-        }
+      if (k0 + TB - 1 > qw) tile(Ks, Vs, k0, std::true_type{});
+      else tile(Ks, Vs, k0, std::false_type{});
     }
     __syncthreads();
   }
@@ -254,7 +274,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(bf16* __restrict__ out, flo
 }
 
 // --------------------------------------------------------------- backward: dQ
-__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
                                                         const bf16* __restrict__ dout,
                                                         const bf16* __restrict__ qkv,
                                                         const bf16* __restrict__ out,
@@ -301,6 +321,35 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv,
     tile_load(rv, vbase, ld, TB, T);
   }
   __syncthreads();
+  // One 64-key tile for this wave's 32 queries; MASK on the tiles that reach
+  // past the wave's first query.
+  auto dq_tile = [&](const bf16* Ks, const bf16* Vs, int k0, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s);
+        dp = mfma(frag_rows(Vs, t * 32 + l32, ks, h2), df[ks], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_(__builtin_fmaf(s[r], c, -L2));
+        if constexpr (MASK) {
+          if (k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
+        }
+        s[r] = p * (dp[r] - Dq);  // dS^T
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t sb = pack_b(s, u);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+          dq[dt] = mfma(frag_tr(Ks, dt * 32, t * 32 + 16 * u, lane), sb, dq[dt]);
+      }
+    }
+  };
   for (int kb = 0; kb < nkb; ++kb) {
     const bf16* Ks = smem + (kb & 1) * 2 * TILE;
     const bf16* Vs = Ks + TILE;
@@ -315,29 +364,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv,
     }
     const int k0 = kb * TB;
     if (k0 <= qw + 31 && qw < T) {
-      const bool diag = k0 + TB - 1 > qw;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x16_t s = zero16(), dp = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          s = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s);
-          dp = mfma(frag_rows(Vs, t * 32 + l32, ks, h2), df[ks], dp);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = exp2_(s[r] * c - L2);
-          if (diag && k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
-          s[r] = p * (dp[r] - Dq);  // dS^T
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t sb = pack_b(s, u);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt)
-            dq[dt] = mfma(frag_tr(Ks, dt * 32, t * 32 + 16 * u, lane), sb, dq[dt]);
-        }
-      }
+      if (k0 + TB - 1 > qw) dq_tile(Ks, Vs, k0, std::true_type{});
+      else dq_tile(Ks, Vs, k0, std::false_type{});
     }
     __syncthreads();
   }
@@ -395,6 +423,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       LD[stage][1][threadIdx.x] = dsv;
     }
   };
+  // One 64-query tile for this wave's 32 keys; MASK on the tiles whose
+  // first queries precede some of the wave's keys.
+  auto dkv_tile = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, int qs0,
+                      auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = mfma(frag_rows(Qs, t * 32 + l32, ks, h2), kf[ks], s);
+        dp = mfma(frag_rows(Os, t * 32 + l32, ks, h2), vf[ks], dp);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rowb = t * 32 + 8 * g + 4 * h2;  // query rows rowb .. rowb+3 of the tile
+        const float4 L4 = *reinterpret_cast<const float4*>(Ls + rowb);
+        const float4 D4 = *reinterpret_cast<const float4*>(Ds + rowb);
+        const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          float p = exp2_(__builtin_fmaf(s[r], c, -Lv[j]));
+          if constexpr (MASK) {
+            if (qs0 + rowb + j < mykey) p = 0.f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - Dv[j]);  // dS
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t pb = pack_b(s, u);
+        bf16x8_t sb = pack_b(dp, u);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          dv[dt] = mfma(frag_tr(Os, dt * 32, t * 32 + 16 * u, lane), pb, dv[dt]);
+          dk[dt] = mfma(frag_tr(Qs, dt * 32, t * 32 + 16 * u, lane), sb, dk[dt]);
+        }
+      }
+    }
+  };
   gload(qb0);
   sstore(0);
   if (qb0 + 1 < nqb) gload(qb0 + 1);
@@ -411,41 +481,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const int qs0 = qb * TB;
     if (qs0 + TB - 1 >= kw && kw < T) {
-      const bool diag = qs0 < kw + 31;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x16_t s = zero16(), dp = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          s = mfma(frag_rows(Qs, t * 32 + l32, ks, h2), kf[ks], s);
-          dp = mfma(frag_rows(Os, t * 32 + l32, ks, h2), vf[ks], dp);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rowb = t * 32 + 8 * g + 4 * h2;  // query rows rowb .. rowb+3 of the tile
-          const float4 L4 = *reinterpret_cast<const float4*>(Ls + rowb);
-          const float4 D4 = *reinterpret_cast<const float4*>(Ds + rowb);
-          const float Lv[4] = {L4.x, L4.y, L4.z, L4.w}, Dv[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * g + j;
-            float p = exp2_(s[r] * c - Lv[j]);
-            if (diag && qs0 + rowb + j < mykey) p = 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - Dv[j]);  // dS
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8_t pb = pack_b(s, u);
-          bf16x8_t sb = pack_b(dp, u);
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            dv[dt] = mfma(frag_tr(Os, dt * 32, t * 32 + 16 * u, lane), pb, dv[dt]);
-            dk[dt] = mfma(frag_tr(Qs, dt * 32, t * 32 + 16 * u, lane), sb, dk[dt]);
-          }
-        }
-      }
+      if (qs0 < kw + 31) dkv_tile(Qs, Os, Ls, Ds, qs0, std::true_type{});
+      else dkv_tile(Qs, Os, Ls, Ds, qs0, std::false_type{});
     }
     __syncthreads();
   }
