@@ -167,9 +167,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bf16* __restrict__ out, float* __restrict__ lse, const bf16* __restrict__ qkv, int T, int H,
     int nqb) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
+  // head-major logical order, longest query block first within a head, so
+  // that the blocks of one head run on one XCD and share its L2
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = nqb - 1 - pid % nqb;
+  const int bh = pid / nqb, b = bh / H, hh = bh % H;
   const int C = H * HD;
   const int64_t ld = 3LL * C;
   const bf16* base = qkv + (int64_t)b * T * ld;
@@ -281,9 +285,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                         const float* __restrict__ lse, int T, int H,
                                                         int nqb) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
+  // head-major logical order, longest query block first within a head, so
+  // that the blocks of one head run on one XCD and share its L2
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = nqb - 1 - pid % nqb;
+  const int bh = pid / nqb, b = bh / H, hh = bh % H;
   const int C = H * HD;
   const int64_t ld = 3LL * C;
   const bf16* base = qkv + (int64_t)b * T * ld;
@@ -384,14 +392,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                          const float* __restrict__ lse, int T, int H) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][Q | dO]
   __shared__ __attribute__((aligned(16))) float LD[2][2][TB];   // [stage][L | D]
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64, h2 = lane / 32, l32 = lane % 32;
-  const int bh = blockIdx.y, b = bh / H, hh = bh % H;
+  const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
+  // head-major logical order, longest key block (the first) first
+  const int nkb_total = (int)cdiv(T, WQ);
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  const int kblk = pid % nkb_total;
+  const int bh = pid / nkb_total, b = bh / H, hh = bh % H;
   const int C = H * HD;
   const int64_t ld = 3LL * C;
   const bf16* base = qkv + (int64_t)b * T * ld;
   const bf16* qbase = base + hh * HD;
   const bf16* dobase = dout + (int64_t)b * T * C + hh * HD;
-  const int k0w = blockIdx.x * WQ, kw = k0w + wave * 32, mykey = kw + l32;
+  const int k0w = kblk * WQ, kw = k0w + wave * 32, mykey = kw + l32;
   const bool kvalid = mykey < T;
   const float c = 0.125f * LOG2E;
 
@@ -423,11 +436,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       LD[stage][1][threadIdx.x] = dsv;
     }
   };
-  // One 64-query tile for this wave's 32 keys; MASK on the tiles whose
+  // One 64-query tile for this wave's 32 keys; diag on the tiles whose
   // first queries precede some of the wave's keys.
   auto dkv_tile = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, int qs0,
-                      auto mask_c) {
-    constexpr bool MASK = decltype(mask_c)::value;
+                      bool diag) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16_t s = zero16(), dp = zero16();
@@ -446,9 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
           float p = exp2_(__builtin_fmaf(s[r], c, -Lv[j]));
-          if constexpr (MASK) {
-            if (qs0 + rowb + j < mykey) p = 0.f;
-          }
+          if (diag && qs0 + rowb + j < mykey) p = 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - Dv[j]);  // dS
         }
@@ -481,8 +491,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const int qs0 = qb * TB;
     if (qs0 + TB - 1 >= kw && kw < T) {
-      if (qs0 < kw + 31) dkv_tile(Qs, Os, Ls, Ds, qs0, std::true_type{});
-      else dkv_tile(Qs, Os, Ls, Ds, qs0, std::false_type{});
+      dkv_tile(Qs, Os, Ls, Ds, qs0, qs0 < kw + 31);
     }
     __syncthreads();
   }
@@ -503,7 +512,7 @@ bool attention_mfma_supported(int dt, int hd) { return dt == BF16 && hd == HD; }
 hipError_t attention_forward_mfma(void* out, float* lse, const void* qkv, int B, int T, int H,
                                   hipStream_t s) {
   const int nqb = (int)cdiv(T, WQ);
-  dim3 grid((unsigned)nqb, (unsigned)(B * H));
+  dim3 grid((unsigned)(nqb * B * H));
   attn_fwd_mfma<<<grid, 256, 0, s>>>((bf16*)out, lse, (const bf16*)qkv, T, H, nqb);
   return hipGetLastError();
 }
@@ -512,7 +521,7 @@ hipError_t attention_backward_mfma(void* dqkv, const void* dout, const void* qkv
                                    const float* lse, float* Dbuf, int B, int T, int H,
                                    hipStream_t s) {
   const int nb = (int)cdiv(T, WQ);
-  dim3 grid((unsigned)nb, (unsigned)(B * H));
+  dim3 grid((unsigned)(nb * B * H));
   attn_bwd_dq_mfma<<<grid, 256, 0, s>>>((bf16*)dqkv, Dbuf, (const bf16*)dout, (const bf16*)qkv,
                                         (const bf16*)out, lse, T, H, nb);
   attn_bwd_dkv_mfma<<<grid, 256, 0, s>>>((bf16*)dqkv, Dbuf, (const bf16*)dout, (const bf16*)qkv,

@@ -79,5 +79,19 @@ __device__ __forceinline__ float gelu_grad_f(float h) {
   return __builtin_fmaf(k * h * s * (1.0f - s), __builtin_fmaf(3.0f * 0.044715f * h, h, 1.0f), s);
 }
 
+// Workgroups are dealt to the 8 XCDs of the chip round-robin by id, and each
+// XCD has its own L2.  xcd_remap turns the hardware id into a logical index
+// such that every XCD receives one contiguous range of logical indices (the
+// first nblocks % 8 XCDs one more than the others), so that neighbouring
+// logical workgroups share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int NX = 8;
+  const int xcd = bid % NX, local = bid / NX;
+  const int per = (nblocks + NX - 1) / NX;
+  const int tall = nblocks % NX;
+  if (tall == 0 || xcd < tall) return xcd * per + local;
+  return tall * per + (xcd - tall) * (per - 1) + local;
+}
+
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }

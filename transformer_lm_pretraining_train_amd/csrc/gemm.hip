@@ -445,14 +445,7 @@ __device__ __forceinline__ void interleave_mfma_reads() {
 
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
                                             int& tn) {
-  // XCD-major renumbering: consecutive workgroup ids go round-robin over the 8 XCDs
-  const int nx = 8;
-  int xcd = bid % nx, local = bid / nx;
-  int per = (nblocks + nx - 1) / nx;
-  int tall = nblocks % nx;
-  int pid;
-  if (tall == 0 || xcd < tall) pid = xcd * per + local;
-  else pid = tall * per + (xcd - tall) * (per - 1) + local;
+  const int pid = xcd_remap(bid, nblocks);
   // grouped order: 8 tile-rows at a time, column-major inside a group
   const int G = 8;
   int in_group = G * tiles_n;
