@@ -204,42 +204,48 @@ hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const 
 }
 
 // Backward: per row, g = dy * w, xhat = (x - mean) rstd,
-// dx = rstd (g - mean(g) - xhat mean(g xhat)); dres += dx.
-// Each workgroup handles LNB_ROWS rows and writes partial column sums of
-// dy*xhat and dy to scratch[block][2][C]; a second kernel adds them up.
+// dx = rstd (g - mean(g) - xhat mean(g xhat)); dres = dx (first) or
+// dres += dx.  Each workgroup handles LNB_ROWS rows and writes partial
+// column sums of dy*xhat, of dy and of the new dres (the bias gradient of
+// the linear layer whose output is that residual) to
+// scratch[block][3][C]; column_partials_reduce adds them up.  NCH: 8-column
+// chunks per lane (C <= 512 NCH), so that no registers are spent on
+// columns that do not exist.
 constexpr int LNB_ROWS = 32;
 
-template <class T>
+template <class T, int NCH>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     T* __restrict__ dres, float* __restrict__ partial, const T* __restrict__ dy,
     const T* __restrict__ inp, const float* __restrict__ mean, const float* __restrict__ rstd,
-    const float* __restrict__ w, int M, int C) {
-  extern __shared__ float red[];  // [2][C]
-  int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  int nch = C / 8;
-  float dwacc[LN_MAXCH][8], dbacc[LN_MAXCH][8];
+    const float* __restrict__ w, int M, int C, int accumulate) {
+  extern __shared__ float red[];  // [3][C]
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int nch = C / 8;
+  float dwacc[NCH][8], dbacc[NCH][8], doacc[NCH][8];
 #pragma unroll
-  for (int j = 0; j < LN_MAXCH; ++j)
+  for (int j = 0; j < NCH; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dwacc[j][i] = dbacc[j][i] = 0.f;
+    for (int i = 0; i < 8; ++i) dwacc[j][i] = dbacc[j][i] = doacc[j][i] = 0.f;
 
-  int row0 = blockIdx.x * LNB_ROWS;
+  const int row0 = blockIdx.x * LNB_ROWS;
   for (int r = wave; r < LNB_ROWS; r += 4) {
-    int row = row0 + r;
+    const int row = row0 + r;
     if (row >= M) break;
-    float mu = mean[row], rs = rstd[row];
+    const float mu = mean[row], rs = rstd[row];
     const T* x = inp + (int64_t)row * C;
     const T* g = dy + (int64_t)row * C;
-    float xh[LN_MAXCH][8], gw[LN_MAXCH][8];
+    T* d = dres + (int64_t)row * C;
+    float xh[NCH][8], gw[NCH][8], dv[NCH][8];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int j = 0; j < LN_MAXCH; ++j) {
-      int ch = lane + 64 * j;
+    for (int j = 0; j < NCH; ++j) {
+      const int ch = lane + 64 * j;
       if (ch < nch) {
         float xv[8], gv[8], wv[8];
         load8(x + ch * 8, xv);
         load8(g + ch * 8, gv);
         load8(w + ch * 8, wv);
+        if (accumulate) load8(d + ch * 8, dv[j]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           xh[j][i] = (xv[i] - mu) * rs;
@@ -248,21 +254,22 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
           s2 += gw[j][i] * xh[j][i];
           dwacc[j][i] += gv[i] * xh[j][i];
           dbacc[j][i] += gv[i];
+          if (!accumulate) dv[j][i] = 0.f;
         }
       }
     }
     s1 = wave_sum(s1) / C;
     s2 = wave_sum(s2) / C;
-    T* d = dres + (int64_t)row * C;
 #pragma unroll
-    for (int j = 0; j < LN_MAXCH; ++j) {
-      int ch = lane + 64 * j;
+    for (int j = 0; j < NCH; ++j) {
+      const int ch = lane + 64 * j;
       if (ch < nch) {
-        float dv[8];
-        load8(d + ch * 8, dv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dv[i] += rs * (gw[j][i] - s1 - xh[j][i] * s2);
-        store8(d + ch * 8, dv);
+        for (int i = 0; i < 8; ++i) {
+          dv[j][i] += rs * (gw[j][i] - s1 - xh[j][i] * s2);
+          doacc[j][i] += dv[j][i];
+        }
+        store8(d + ch * 8, dv[j]);
       }
     }
   }
@@ -270,18 +277,20 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   for (int wv = 0; wv < 4; ++wv) {
     if (wave == wv) {
 #pragma unroll
-      for (int j = 0; j < LN_MAXCH; ++j) {
-        int ch = lane + 64 * j;
+      for (int j = 0; j < NCH; ++j) {
+        const int ch = lane + 64 * j;
         if (ch < nch) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            int c = ch * 8 + i;
+            const int c = ch * 8 + i;
             if (wv == 0) {
               red[c] = dwacc[j][i];
               red[C + c] = dbacc[j][i];
+              red[2 * C + c] = doacc[j][i];
             } else {
               red[c] += dwacc[j][i];
               red[C + c] += dbacc[j][i];
+              red[2 * C + c] += doacc[j][i];
             }
           }
         }
@@ -289,52 +298,73 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     }
     __syncthreads();
   }
-  float* dst = partial + (int64_t)blockIdx.x * 2 * C;
-  for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) dst[c] = red[c];
+  float* dst = partial + (int64_t)blockIdx.x * 3 * C;
+  for (int c = threadIdx.x; c < 3 * C; c += blockDim.x) dst[c] = red[c];
 }
 
-// out0[c] += sum_b partial[b * stride + c] for c < C, and out1[c - C] for
-// C <= c < 2C when out1 is given.  256 threads = 32 columns x 8 groups of
-// partials; each group sums every 8th partial, then the 8 group sums are
-// added in a fixed order.
-__global__ __launch_bounds__(256) void column_partials_reduce_kernel(float* __restrict__ out0,
-                                                                     float* __restrict__ out1,
-                                                                     const float* __restrict__ partial,
-                                                                     int nb, int C, int stride) {
-  __shared__ float red[8][33];
-  const int lc = threadIdx.x % 32, g = threadIdx.x / 32;
-  const int c = blockIdx.x * 32 + lc;
-  const int total = out1 ? 2 * C : C;
-  float acc = 0.f;
-  if (c < total)
-    for (int b = g; b < nb; b += 8) acc += partial[(int64_t)b * stride + c];
-  red[g][lc] = acc;
+// out_k[c] += sum_b partial[b * stride + k * C + c] for each non-null out_k
+// (k = 0, 1, 2), summed in a fixed order.  A workgroup covers 64 columns of
+// the concatenated outputs with 16 float4 lanes x 16 groups of partial rows
+// (group g sums rows g, g+16, ...); the 16 group sums are added in order.
+__global__ __launch_bounds__(256) void column_partials_reduce_kernel(
+    float* __restrict__ out0, float* __restrict__ out1, float* __restrict__ out2,
+    const float* __restrict__ partial, int nb, int C, int stride, int ncols) {
+  __shared__ float4 red[16][17];
+  const int q = threadIdx.x % 16, g = threadIdx.x / 16;
+  const int c = blockIdx.x * 64 + 4 * q;  // first of 4 columns (C % 4 == 0)
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < ncols) {
+#pragma unroll 4
+    for (int b = g; b < nb; b += 16) {
+      const float4 v = *reinterpret_cast<const float4*>(partial + (int64_t)b * stride + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  }
+  red[g][q] = acc;
   __syncthreads();
-  if (g == 0 && c < total) {
-    float t = 0.f;
+  if (g == 0 && c < ncols) {
+    float4 t = red[0][q];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) t += red[k][lc];
-    if (c < C)
-      out0[c] += t;
-    else
-      out1[c - C] += t;
+    for (int k = 1; k < 16; ++k) {
+      const float4 v = red[k][q];
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+    }
+    const int k = c / C, cc = c % C;
+    float* o = k == 0 ? out0 : k == 1 ? out1 : out2;
+    if (o) {
+      float4* op = reinterpret_cast<float4*>(o + cc);
+      float4 cur = *op;
+      cur.x += t.x; cur.y += t.y; cur.z += t.z; cur.w += t.w;
+      *op = cur;
+    }
   }
 }
 
 size_t layernorm_backward_scratch_bytes(int M, int C) {
-  return (size_t)cdiv(M, LNB_ROWS) * 2 * C * sizeof(float);
+  return (size_t)cdiv(M, LNB_ROWS) * 3 * C * sizeof(float);
 }
 
-hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, const void* dy,
-                              const void* inp, const float* mean, const float* rstd,
-                              const float* w, int M, int C, void* scratch, hipStream_t s) {
+hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, float* dsum,
+                              bool accumulate, const void* dy, const void* inp, const float* mean,
+                              const float* rstd, const float* w, int M, int C, void* scratch,
+                              hipStream_t s) {
   if (C % 8 != 0 || C > 8 * 64 * LN_MAXCH) return hipErrorInvalidValue;
-  int nb = (int)cdiv(M, LNB_ROWS);
+  const int nb = (int)cdiv(M, LNB_ROWS);
   float* partial = (float*)scratch;
-  DISPATCH_DT(dt, layernorm_bwd_kernel<T><<<nb, 256, 2 * C * sizeof(float), s>>>(
-                      (T*)dres, partial, (const T*)dy, (const T*)inp, mean, rstd, w, M, C));
-  column_partials_reduce_kernel<<<grid_for(2 * C, 32), 256, 0, s>>>(dw, db, partial, nb, C,
-                                                                     2 * C);
+  const int nch = (int)cdiv(C / 8, 64);
+  const size_t lds = 3 * C * sizeof(float);
+#define LNB(NC)                                                                                \
+  DISPATCH_DT(dt, layernorm_bwd_kernel<T, NC><<<nb, 256, lds, s>>>(                            \
+                      (T*)dres, partial, (const T*)dy, (const T*)inp, mean, rstd, w, M, C,      \
+                      accumulate ? 1 : 0))
+  if (nch == 1) LNB(1);
+  else if (nch == 2) LNB(2);
+  else if (nch == 3) LNB(3);
+  else LNB(4);
+#undef LNB
+  const int ncols = dsum ? 3 * C : 2 * C;
+  column_partials_reduce_kernel<<<grid_for(ncols, 64), 256, 0, s>>>(dw, db, dsum, partial, nb, C,
+                                                                     3 * C, ncols);
   return hipGetLastError();
 }
 
@@ -383,8 +413,8 @@ hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ld
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)cdiv(M, BG_ROWS));
   float* partial = (float*)scratch;
   DISPATCH_DT(dt, bias_grad_kernel<T><<<grid, 256, 0, s>>>(partial, (const T*)dy, M, N, ldy));
-  column_partials_reduce_kernel<<<grid_for(N, 32), 256, 0, s>>>(db, nullptr, partial,
-                                                                 (int)grid.y, N, N);
+  column_partials_reduce_kernel<<<grid_for(N, 64), 256, 0, s>>>(db, nullptr, nullptr, partial,
+                                                                 (int)grid.y, N, N, N);
   return hipGetLastError();
 }
 

@@ -24,11 +24,14 @@ hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32
 // ---- LayerNorm
 hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,
                              const float* w, const float* b, int M, int C, float eps, hipStream_t s);
-// dres += dx; dw, db += column sums (two-stage, partials in scratch).
+// dres = dx (accumulate false) or dres += dx; dw, db += column sums of
+// dy*xhat and dy; dsum (if not null) += column sums of the new dres.
+// Two-stage, partials in scratch.
 size_t layernorm_backward_scratch_bytes(int M, int C);
-hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, const void* dy,
-                              const void* inp, const float* mean, const float* rstd, const float* w,
-                              int M, int C, void* scratch, hipStream_t s);
+hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, float* dsum,
+                              bool accumulate, const void* dy, const void* inp, const float* mean,
+                              const float* rstd, const float* w, int M, int C, void* scratch,
+                              hipStream_t s);
 
 // ---- bias gradient: db[n] += sum_m dy[m, n] (two-stage, partials in scratch)
 size_t bias_grad_scratch_bytes(int M, int N);

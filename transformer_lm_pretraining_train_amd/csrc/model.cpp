@@ -535,9 +535,13 @@ int gpt2_backward(gpt2_model* md) {
   LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->logits, md->ldl, md->wt(Ly.wte), C,
               epi(EPI_STORE, md->dbuf_c, C), s));
   const void* xfinal = md->L > 0 ? md->act[md->L - 1].res3 : md->encoded;
-  LAUNCH(fill_f32((float*)md->dres, 0.f, md->M * C * (int64_t)dsize(dt) / 4, s));
-  LAUNCH(layernorm_backward(dt, md->dres, G + Ly.lnf_w, G + Ly.lnf_b, md->dbuf_c, xfinal,
-                            md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C, md->scratch, s));
+  // The column sums of each residual gradient a LayerNorm backward produces
+  // are the bias gradient of the linear layer that wrote that residual:
+  // fc-proj of the layer below (res3) or proj of the same layer (res2).
+  float* fcp_b_below = md->L > 0 ? G + Ly.layers[md->L - 1].fcp_b : nullptr;
+  LAUNCH(layernorm_backward(dt, md->dres, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
+                            md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
+                            md->scratch, s));
   for (int l = md->L - 1; l >= 0; --l) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
@@ -545,7 +549,6 @@ int gpt2_backward(gpt2_model* md) {
     // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
     LAUNCH(gemm(dt, false, false, C, 4 * C, M, md->dres, C, a.fchg, 4 * C,
                 epi(EPI_ACC_F32, G + o.fcp_w, 4 * C), s, md->gemm_ws, md->gemm_ws_bytes));
-    LAUNCH(bias_grad(dt, G + o.fcp_b, md->dres, M, C, C, md->scratch, s));
     Epilogue e = epi(EPI_GELU_BWD, md->dbuf_4c, 4 * C);
     e.aux = a.fch;
     e.ldx = 4 * C;
@@ -556,12 +559,12 @@ int gpt2_backward(gpt2_model* md) {
     LAUNCH(bias_grad(dt, G + o.fc_b, md->dbuf_4c, M, 4 * C, 4 * C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, 4 * C, md->dbuf_4c, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln2_w, G + o.ln2_b, md->dbuf_c, a.res2,
-                              a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C, md->scratch, s));
+    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
+                              md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
+                              md->scratch, s));
     // attention output projection: res2 = x + atty proj_w^T + proj_b
     LAUNCH(gemm(dt, false, false, C, C, M, md->dres, C, a.atty, C,
                 epi(EPI_ACC_F32, G + o.proj_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
-    LAUNCH(bias_grad(dt, G + o.proj_b, md->dres, M, C, C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, C, md->dres, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
     TIMED(GPT2_TIMER_ATTN_BWD, attention_backward(dt, md->dqkv, md->dbuf_c, a.qkv, a.atty, a.lse,
@@ -572,7 +575,8 @@ int gpt2_backward(gpt2_model* md) {
     LAUNCH(bias_grad(dt, G + o.qkv_b, md->dqkv, M, 3 * C, 3 * C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, 3 * C, md->dqkv, 3 * C, md->wt(o.qkv_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln1_w, G + o.ln1_b, md->dbuf_c, xin,
+    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln1_w, G + o.ln1_b,
+                              l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c, xin,
                               a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, md->scratch, s));
   }
   // embeddings
