@@ -198,25 +198,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     tile_load(rv, vbase, ld, TB, T);
   }
   __syncthreads();
-  // One 64-key tile for this wave's 32 queries; MASK on the tiles that reach
-  // past the wave's first query.
-  auto tile = [&](const bf16* Ks, const bf16* Vs, int k0, auto mask_c) {
-    constexpr bool MASK = decltype(mask_c)::value;
+  // One 64-key tile for this wave's 32 queries.
+  auto tile = [&](const bf16* Ks, const bf16* Vs, int k0, bool diag) {
     f32x16_t s[2] = {zero16(), zero16()};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int t = 0; t < 2; ++t) s[t] = mfma(frag_rows(Ks, t * 32 + l32, ks, h2), qf[ks], s[t]);
-    float mx = -INFINITY;
+    if (diag) {  // wave-uniform: only the tiles that reach past the first query
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (MASK) {
+        for (int r = 0; r < 16; ++r)
           if (k0 + t * 32 + acc_row(r, h2) > myq) s[t][r] = -INFINITY;
-        }
-        mx = fmaxf(mx, s[t][r]);
-      }
+    }
+    // row maximum as a tree (short dependency chains)
+    float m8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      m8[i] = fmaxf(fmaxf(s[i / 4][4 * (i % 4)], s[i / 4][4 * (i % 4) + 1]),
+                    fmaxf(s[i / 4][4 * (i % 4) + 2], s[i / 4][4 * (i % 4) + 3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
+    float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
     // move the reference only when this tile exceeds it by more than 2^8
     const bool move = mx > m + RESCALE_LOG2;
@@ -228,16 +232,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       o[0] *= alpha;
       o[1] *= alpha;
     }
-    float ps = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_(__builtin_fmaf(s[t][r], c, -m));
         s[t][r] = p;
-        ps += p;
+        ps[r % 4] += p;
       }
-    l += ps;
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -248,9 +252,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           o[dt] = mfma(frag_tr(Vs, dt * 32, t * 32 + 16 * u, lane), pb, o[dt]);
       }
   };
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
-    const bf16* Vs = Ks + TILE;
+  // stage tile kb+1 into LDS and start loading tile kb+2
+  auto advance = [&](int kb) {
     if (kb + 1 < nkb) {
       bf16* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
       tile_store(rk, nxt);
@@ -260,11 +263,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         tile_load(rv, vbase, ld, (kb + 2) * TB, T);
       }
     }
-    const int k0 = kb * TB;
-    if (k0 <= qw + 31 && qw < T) {
-      if (k0 + TB - 1 > qw) tile(Ks, Vs, k0, std::true_type{});
-      else tile(Ks, Vs, k0, std::false_type{});
-    }
+  };
+  // Tiles every wave of the block needs (those up to the first wave's last
+  // query) run unconditionally, which keeps the accumulators in place; only
+  // the block's last tile can be needed by some waves and not others.
+  const int nall = min(nkb, (q0 + 31) / TB + 1);
+  int kb = 0;
+  for (; kb < nall; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    advance(kb);
+    tile(Ks, Ks + TILE, kb * TB, kb * TB + TB - 1 > qw);
+    __syncthreads();
+  }
+  for (; kb < nkb; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    advance(kb);
+    if (kb * TB <= qw + 31) tile(Ks, Ks + TILE, kb * TB, true);
     __syncthreads();
   }
   l += __shfl_xor(l, 32, 64);
@@ -329,10 +343,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     tile_load(rv, vbase, ld, TB, T);
   }
   __syncthreads();
-  // One 64-key tile for this wave's 32 queries; MASK on the tiles that reach
+  // One 64-key tile for this wave's 32 queries; diag on the tiles that reach
   // past the wave's first query.
-  auto dq_tile = [&](const bf16* Ks, const bf16* Vs, int k0, auto mask_c) {
-    constexpr bool MASK = decltype(mask_c)::value;
+  auto dq_tile = [&](const bf16* Ks, const bf16* Vs, int k0, bool diag) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16_t s = zero16(), dp = zero16();
@@ -344,9 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = exp2_(__builtin_fmaf(s[r], c, -L2));
-        if constexpr (MASK) {
-          if (k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
-        }
+        if (diag && k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
         s[r] = p * (dp[r] - Dq);  // dS^T
       }
 #pragma unroll
@@ -358,9 +369,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
-    const bf16* Vs = Ks + TILE;
+  auto advance = [&](int kb) {
     if (kb + 1 < nkb) {
       bf16* nxt = smem + ((kb + 1) & 1) * 2 * TILE;
       tile_store(rk, nxt);
@@ -370,11 +379,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         tile_load(rv, vbase, ld, (kb + 2) * TB, T);
       }
     }
-    const int k0 = kb * TB;
-    if (k0 <= qw + 31 && qw < T) {
-      if (k0 + TB - 1 > qw) dq_tile(Ks, Vs, k0, std::true_type{});
-      else dq_tile(Ks, Vs, k0, std::false_type{});
-    }
+  };
+  // as in the forward: unconditional tiles first, then the block's last one
+  const int nall = min(nkb, (q0 + 31) / TB + 1);
+  int kb = 0;
+  for (; kb < nall; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    advance(kb);
+    dq_tile(Ks, Ks + TILE, kb * TB, kb * TB + TB - 1 > qw);
+    __syncthreads();
+  }
+  for (; kb < nkb; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    advance(kb);
+    if (kb * TB <= qw + 31) dq_tile(Ks, Ks + TILE, kb * TB, true);
     __syncthreads();
   }
   if (qvalid) {
@@ -479,22 +497,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   sstore(0);
   if (qb0 + 1 < nqb) gload(qb0 + 1);
   __syncthreads();
-  for (int qb = qb0; qb < nqb; ++qb) {
+  // iteration qb: stage tile qb+1, load qb+2, multiply tile qb.  Only the
+  // first query tile (it starts at the block's first key) can be skipped by
+  // some waves; the rest run unconditionally, keeping the accumulators in place.
+  auto step = [&](int qb, bool need) {
     const int stage = (qb - qb0) & 1;
     const bf16* Qs = smem + stage * 2 * TILE;
-    const bf16* Os = Qs + TILE;
-    const float* Ls = LD[stage][0];
-    const float* Ds = LD[stage][1];
     if (qb + 1 < nqb) {
       sstore(stage ^ 1);
       if (qb + 2 < nqb) gload(qb + 2);
     }
     const int qs0 = qb * TB;
-    if (qs0 + TB - 1 >= kw && kw < T) {
-      dkv_tile(Qs, Os, Ls, Ds, qs0, qs0 < kw + 31);
-    }
+    if (need) dkv_tile(Qs, Qs + TILE, LD[stage][0], LD[stage][1], qs0, qs0 < kw + 31);
     __syncthreads();
-  }
+  };
+  if (qb0 < nqb) step(qb0, qb0 * TB + TB - 1 >= kw);
+  for (int qb = qb0 + 1; qb < nqb; ++qb) step(qb, true);
   if (kvalid) {
     bf16* dst = dqkv + ((int64_t)b * T + mykey) * ld + hh * HD;
 #pragma unroll
