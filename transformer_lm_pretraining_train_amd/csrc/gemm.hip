@@ -361,8 +361,14 @@ struct BigOperand {
   struct Src {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t voff[NI];  // byte offset of each load's vector for k0 = 0, or kOOB
-    int kofs[NI];       // its k offset inside a tile (masks a ragged last tile)
   };
+
+  // k offset inside a tile of the vector that load q of this lane fetches
+  __device__ __forceinline__ static int kofs(int q, int wave, int lane) {
+    const int slot = (wave + NW * q) * 64 + lane;
+    if constexpr (KMAJOR) return 8 * ((slot & 7) ^ swz(slot >> 3));
+    else return slot / CPR;
+  }
 
   // P: the operand, ld: its row pitch in elements, row0: first output row of
   // this tile, rows_total: rows of the output dimension, K: the k extent.
@@ -380,12 +386,10 @@ struct BigOperand {
         const int row = slot >> 3;
         const int ko = 8 * ((slot & 7) ^ swz(row));
         st.voff[q] = row0 + row < rows_total ? (uint32_t)(((int64_t)row * ld + ko) * 2) : kOOB;
-        st.kofs[q] = ko;
       } else {
         const int krow = slot / CPR;
         const int c = 8 * mlog(krow, slot % CPR);
         st.voff[q] = row0 + c < rows_total ? (uint32_t)(((int64_t)krow * ld + c) * 2) : kOOB;
-        st.kofs[q] = krow;
       }
     }
   }
@@ -395,11 +399,11 @@ struct BigOperand {
   // read as zeros.
   template <bool TAIL>
   __device__ __forceinline__ static void load(bf16* __restrict__ S, const Src& st, int64_t ld,
-                                              int k0, int kend, int wave) {
+                                              int k0, int kend, int wave, int lane) {
     const uint32_t soff = (uint32_t)(KMAJOR ? (int64_t)k0 * 2 : (int64_t)k0 * ld * 2);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
-      const uint32_t v = TAIL && k0 + st.kofs[q] >= kend ? kOOB : st.voff[q];
+      const uint32_t v = TAIL && k0 + kofs(q, wave, lane) >= kend ? kOOB : st.voff[q];
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist only for the GPU target
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           st.rs, (__attribute__((address_space(3))) void*)(S + (wave + NW * q) * 512), 16, v, soff, 0, 0);
@@ -443,9 +447,10 @@ __device__ __forceinline__ void interleave_mfma_reads() {
   }
 }
 
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
-                                            int& tn) {
-  const int pid = xcd_remap(bid, nblocks);
+// Output tile of logical index pid: groups of 8 tile-rows, column-major
+// inside a group, so that tiles with neighbouring indices share operand
+// panels.
+__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
   // grouped order: 8 tile-rows at a time, column-major inside a group
   const int G = 8;
   int in_group = G * tiles_n;
@@ -489,8 +494,13 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
   const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: LDS bases in SGPRs
   const int wm = wave / 2, wn = wave % 2;
+  // Persistent: workgroup w takes logical tiles w, w + G, w + 2G, ... (G
+  // workgroups, at most one per CU), with w numbered XCD-major so that the
+  // tiles an XCD works on at the same time are neighbours and share its L2.
+  const int ntiles = tiles_m * tiles_n;
+  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of(tile, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int kbeg = blockIdx.y * kps;
   const int kend = min(K, kbeg + kps);
@@ -510,11 +520,11 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
   OB::init(srcB, B, ldb, n0, N, K, wave, lane);
   auto issue = [&](bf16* st, int k0) {
     if (k0 + 64 > kend) {
-      OA::template load<true>(st, srcA, lda, k0, kend, wave);
-      OB::template load<true>(st + OA::ELEMS, srcB, ldb, k0, kend, wave);
+      OA::template load<true>(st, srcA, lda, k0, kend, wave, lane);
+      OB::template load<true>(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
     } else {
-      OA::template load<false>(st, srcA, lda, k0, kend, wave);
-      OB::template load<false>(st + OA::ELEMS, srcB, ldb, k0, kend, wave);
+      OA::template load<false>(st, srcA, lda, k0, kend, wave, lane);
+      OB::template load<false>(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
     }
   };
   // Fragments are double-buffered in registers: the LDS reads of k-step s+1
@@ -616,6 +626,8 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
       __builtin_amdgcn_wave_barrier();
     }
   }
+  __syncthreads();  // the next tile's loads overwrite the staging slabs
+  }
 }
 
 // dst[m, n] (fp32, row pitch ldo) += sum over s of part[s][m][n], in order.
@@ -689,7 +701,10 @@ hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, in
                       const bf16* b, int64_t ldb, const Epilogue& e, int splits, hipStream_t s) {
   int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   int kps = (int)round_up(cdiv(K, splits), 64);
-  dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
+  // one workgroup per CU (the LDS use allows no more), each looping over tiles
+  const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+  const int g = (int)(splits > 1 ? ntiles : (ntiles < kCUs ? ntiles : kCUs));
+  dim3 grid((unsigned)g, (unsigned)splits);
 #define GO(AK, BK_) gemm_big_kernel<BM, BN, AK, BK_, MODE><<<grid, BigWaves<BN>::NW * 64, 0, s>>>(M, N, K, a, lda, b, ldb, e, kps, tiles_m, tiles_n)
   if (akm && bkm) GO(true, true);
   else if (akm && !bkm) GO(true, false);
