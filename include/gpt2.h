@@ -77,7 +77,9 @@ typedef struct {
   int32_t seq_len;           /* T */
   int32_t grad_accum_steps;  /* k: backward scales the loss by 1/k */
   int32_t dtype;             /* GPT2_FP32 or GPT2_BF16 (activations + GEMM inputs) */
-  int32_t deterministic;     /* nonzero: no floating-point atomics, bitwise repeatable */
+  int32_t deterministic;     /* accepted either way: no kernel uses floating-point atomics and
+                                every reduction runs in a fixed order, so a step is bitwise
+                                repeatable for a given config and device */
   float ln_eps;              /* LayerNorm eps, 1e-5 */
 } gpt2_config;
 

@@ -67,9 +67,15 @@ def test_workspace_sizes_fit_288gb():
         assert 0 < nb < 200 * 2 ** 30, (name, nb)
 
 
+def test_deterministic_flag_accepted():
+    cfg = g.config_for(synth.workload("tiny"))
+    cfg.deterministic = 1
+    assert g.workspace_bytes(cfg) > 0
+
+
 @pytest.mark.parametrize("field,value", [
     ("n_embd", 100), ("n_head", 7), ("seq_len", 2048), ("padded_vocab_size", 10),
-    ("dtype", 5), ("micro_batch", 0), ("deterministic", 1), ("ln_eps", 0.0)])
+    ("dtype", 5), ("micro_batch", 0), ("ln_eps", 0.0)])
 def test_invalid_configs_rejected(field, value):
     cfg = g.config_for(synth.workload("tiny"))
     setattr(cfg, field, value)

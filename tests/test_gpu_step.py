@@ -290,3 +290,21 @@ def test_kernel_timer_counts_launches_and_leaves_results_unchanged():
     m.set_kernel_timer("none")
     m.forward(to_dev(batches[0][0]), to_dev(batches[0][1]), None)
     assert m.read_kernel_timer() == (0, 0.0)
+
+
+def test_gradients_bitwise_repeatable():
+    # small workload: Zipf tokens, long runs of frequent ids across windows
+    # and chunks of the embedding backward; two identical steps must agree
+    # bit for bit
+    wl, cfg, ocfg, layout, flat, batches = setup_case("small", "bf16", k=2)
+    cfg.deterministic = 1
+    grads = []
+    for _ in range(2):
+        m = g.Model(cfg)
+        m.set_params(to_dev(flat))
+        m.zero_grad()
+        for x, y in batches:
+            m.forward(to_dev(x), to_dev(y), None)
+            m.backward()
+        grads.append(host(m.get_grads()))
+    assert np.array_equal(grads[0], grads[1])

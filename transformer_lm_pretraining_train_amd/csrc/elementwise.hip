@@ -109,32 +109,6 @@ hipError_t encoder_backward_wpe(int dt, float* dwpe, const void* dx, int B, int 
   return hipGetLastError();
 }
 
-// dwte[tok[m], c] += dx[m, c]: fp32 atomics (tokens collide under Zipf).
-template <class T>
-__global__ void encoder_bwd_wte_kernel(float* __restrict__ dwte, const T* __restrict__ dx,
-                                       const int32_t* __restrict__ tok, int M, int C, int V) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int cpr = C / 8;
-  if (idx >= (int64_t)M * cpr) return;
-  int m = (int)(idx / cpr);
-  int c = (int)(idx % cpr) * 8;
-  int id = tok[m];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-  float v[8];
-  load8(dx + (int64_t)m * C + c, v);
-  float* dst = dwte + (int64_t)id * C + c;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) unsafeAtomicAdd(dst + i, v[i]);
-}
-
-hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32_t* tok, int M,
-                                int C, int V, hipStream_t s) {
-  int64_t n = (int64_t)M * (C / 8);
-  DISPATCH_DT(dt, encoder_bwd_wte_kernel<T><<<grid_for(n, 256), 256, 0, s>>>(
-                      dwte, (const T*)dx, tok, M, C, V));
-  return hipGetLastError();
-}
-
 // =========================================================== LayerNorm
 // One wave per row; lane j owns 8-element chunks j, j+64, ... (C % 8 == 0).
 constexpr int LN_MAXCH = 4;  // C <= 8 * 64 * 4 = 2048

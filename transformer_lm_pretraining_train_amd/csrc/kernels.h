@@ -17,9 +17,11 @@ hipError_t encoder_forward(int dt, void* out, const int32_t* tok, const float* w
                            int M, int T, int C, int V, int* err_flag, hipStream_t s);
 hipError_t encoder_backward_wpe(int dt, float* dwpe, const void* dx, int B, int T, int C,
                                 hipStream_t s);
-// dwte[tok[m]] += dx[m] with fp32 atomics (ids clamped to [0, V)).
+// dwte[tok[m]] += dx[m], each token's rows summed in position order through a
+// counting sort of the positions (no float atomics; ids clamped to [0, V)).
+size_t encoder_backward_wte_scratch_bytes(int M, int V, int C);
 hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32_t* tok, int M,
-                                int C, int V, hipStream_t s);
+                                int C, int V, void* scratch, hipStream_t s);
 
 // ---- LayerNorm
 hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,

@@ -118,9 +118,6 @@ int validate(const gpt2_config* c) {
   if ((int64_t)c->micro_batch * c->seq_len > (1 << 24))
     return fail(GPT2_EINVAL, "micro_batch * seq_len too large");
   if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16) return fail(GPT2_EINVAL, "dtype must be 0 or 1");
-  if (c->deterministic)
-    return fail(GPT2_EINVAL,
-                "deterministic mode is not available: the embedding backward uses fp32 atomics");
   if (!(c->ln_eps > 0.f)) return fail(GPT2_EINVAL, "ln_eps must be > 0");
   return GPT2_OK;
 }
@@ -237,6 +234,7 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   size_t sc = layernorm_backward_scratch_bytes((int)M, (int)C);
   sc = std::max(sc, bias_grad_scratch_bytes((int)M, (int)(4 * C)));
   sc = std::max(sc, attention_backward_scratch_bytes(c.micro_batch, c.seq_len, H));
+  sc = std::max(sc, encoder_backward_wte_scratch_bytes((int)M, c.vocab_size, (int)C));
   md.scratch = cv.take(sc);
   size_t gw = 0;
   {
@@ -323,10 +321,8 @@ const char* gpt2_last_error(void) { return g_err.c_str(); }
 
 int64_t gpt2_num_params(const gpt2_config* cfg) {
   if (!cfg) return -1;
-  gpt2_config c = *cfg;
-  c.deterministic = 0;
-  if (validate(&c) != GPT2_OK) return -1;
-  return make_layout(c).total;
+  if (validate(cfg) != GPT2_OK) return -1;
+  return make_layout(*cfg).total;
 }
 
 size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
@@ -336,11 +332,9 @@ size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
 
 int gpt2_param_layout(const gpt2_config* cfg, gpt2_tensor_info* out, int cap) {
   if (!cfg) return fail(GPT2_EINVAL, "config is NULL");
-  gpt2_config c = *cfg;
-  c.deterministic = 0;
-  int rc = validate(&c);
+  int rc = validate(cfg);
   if (rc != GPT2_OK) return rc;
-  Layout L = make_layout(c);
+  Layout L = make_layout(*cfg);
   int n = (int)L.tensors.size();
   if (out) {
     for (int i = 0; i < n && i < cap; ++i) {
@@ -580,7 +574,7 @@ int gpt2_backward(gpt2_model* md) {
                               a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, md->scratch, s));
   }
   // embeddings
-  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, s));
+  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
   LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, md->dres, md->B, md->Tn, C, s));
   return GPT2_OK;
 }
