@@ -131,6 +131,10 @@ def test_gemm_gpt2_124m_shapes_sampled(akm, bkm, M, N, K):
     g.gemm(BF16, akm, bkm, M, N, K, A, A.shape[1], B, B.shape[1], "store", out, N)
     torch.cuda.synchronize()
     rows = np.random.default_rng(M ^ N ^ K).choice(M, 64, replace=False)
+    # the first, middle and last rows, and (wte gradient) both sides of the
+    # row split that runs the tail of the tile grid with split-K
+    extra = [0, M // 2, M - 1] + ([43519, 43520, 50303 - 256] if M == 50304 else [])
+    rows = np.unique(np.concatenate([rows, np.array(extra)]))
     ridx = torch.from_numpy(rows).cuda()
     Am = (A[ridx] if akm else A[:, ridx].T).float().cpu().numpy().astype(np.float64)
     Bm = (B if bkm else B.T).float().cpu().numpy().astype(np.float64)

@@ -18,6 +18,7 @@
 // 128 x 128 x 64, four waves of 64 x 64 (2 x 2 MFMA tiles), next k-tile
 // prefetched into registers while the current one is multiplied.
 // fp32 (the fp32 parity mode): plain LDS-tiled FMA kernel.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -769,8 +770,27 @@ hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const vo
 
 }  // namespace
 
+// Weight-gradient products with more 256 x 256 tiles than CUs but a last
+// round less than half full (the tied-head gradient: 591 tiles on 256 CUs)
+// are cut by rows: the rows that fill whole rounds run unsplit, the rest
+// with split-K, so that the tail costs a fraction of a round.  Returns the
+// rows of the first part, or 0 to run the product whole.
+int acc_row_split(int dt, int M, int N, int K, int mode) {
+  if (dt != BF16 || mode != EPI_ACC_F32) return 0;
+  const Plan p = plan_gemm(M, N, K, mode);
+  if (p.kind != 1 || p.splits != 1) return 0;
+  const int64_t tn = cdiv(N, 256), tiles = cdiv(M, 256) * tn;
+  const int64_t full = tiles / kCUs * kCUs, rest = tiles - full;
+  if (full == 0 || rest == 0 || rest * 2 > kCUs) return 0;
+  const int64_t rows = full / tn * 256;
+  return rows > 0 && rows < M ? (int)rows : 0;
+}
+
 size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode) {
   if (dt != BF16 || mode != EPI_ACC_F32) return 0;
+  const int r = acc_row_split(dt, M, N, K, mode);
+  if (r > 0) return std::max(gemm_workspace_bytes(dt, r, N, K, mode),
+                             gemm_workspace_bytes(dt, M - r, N, K, mode));
   Plan p = plan_gemm(M, N, K, mode);
   if (p.kind == 0 || p.splits <= 1) return 0;
   return (size_t)p.splits * M * N * sizeof(float);
@@ -781,6 +801,16 @@ hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const
                 void* ws, size_t ws_bytes) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dt == BF16 && (lda % 8 != 0 || ldb % 8 != 0)) return hipErrorInvalidValue;
+  if (const int r = acc_row_split(dt, M, N, K, e.mode)) {
+    hipError_t err = launch_mode<EPI_ACC_F32>(dt, a_kmajor, b_kmajor, r, N, K, A, lda, B, ldb, e, s,
+                                              ws, ws_bytes);
+    if (err != hipSuccess) return err;
+    const bf16* A2 = (const bf16*)A + (a_kmajor ? (int64_t)r * lda : (int64_t)r);
+    Epilogue e2 = e;
+    e2.out = (float*)e.out + (int64_t)r * e.ldo;
+    return launch_mode<EPI_ACC_F32>(dt, a_kmajor, b_kmajor, M - r, N, K, A2, lda, B, ldb, e2, s,
+                                    ws, ws_bytes);
+  }
 #define CASE(MD) \
   case MD: return launch_mode<MD>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s, ws, ws_bytes);
   switch (e.mode) {
