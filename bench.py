@@ -28,11 +28,11 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2
 PEAK_HBM_GBS = 8000.0
 
 # HBM traffic of one lm_head forward GEMM launch from two rocprofv3 --pmc runs
-# (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), scaled by what the same
+# (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, mean of six), scaled by what the same
 # counters read for a plain 1 GiB device copy (FETCH_SIZE reads half the
 # bytes copied: factor 2.0; WRITE_SIZE is exact: factor 1.0).  Valid only for
 # the GEMM source it was measured on (first 16 hex digits of its sha256).
-LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "2c5e6b5464da1405", "fetch_kib": 916336, "write_kib": 1609728,
+LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "ed1b2ecabc089502", "fetch_kib": 931690, "write_kib": 1609728,
                    "fetch_factor": 2.0, "write_factor": 1.0}
 
 
