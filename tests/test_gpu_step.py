@@ -26,9 +26,9 @@ from gpu_util import cosine, host, rel_l2, to_dev  # noqa: E402
 LR = 6e-4
 
 
-def setup_case(name, dtype, perturbed=True, k=None, B=None, T=None, Vp=None):
+def setup_case(name, dtype, perturbed=True, k=None, B=None, T=None, Vp=None, **shape):
     wl = synth.workload(name)
-    over = {}
+    over = dict(shape)
     if k is not None:
         over["grad_accum"] = k
     if B is not None:
@@ -186,6 +186,36 @@ def test_tiny_bf16_step_matches_oracle():
     G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
     for n in G:
         assert cosine(G[n], O[n]) >= 0.99, n
+
+
+@pytest.mark.parametrize("C,H", [(256, 4), (512, 8)])
+def test_fp32_width_multiple_of_256_matches_oracle(C, H):
+    """Widths 256 and 512 (64-wide heads) take the half-wave LayerNorm
+    backward; fp32 tolerances as for the tiny model."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "fp32", B=2, n_layer=2,
+                                                      n_embd=C, n_head=H)
+    print(f"fp32 C={C} H={H}", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    assert abs(gs[0]["losses"][0] - orr["losses"][0]) <= 1e-4 * orr["losses"][0]
+    G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
+    for n in G:
+        assert rel_l2(G[n], O[n]) <= 1e-3, (n, rel_l2(G[n], O[n]))
+    assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-3
+
+
+def test_bf16_width_768_matches_oracle():
+    """The GPT-2 124M width (12 heads of 64) in bf16 on a one-layer model."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "bf16", B=2, n_layer=1,
+                                                      n_embd=768, n_head=12)
+    print("bf16 C=768", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    assert abs(gs[0]["losses"][0] - orr["losses"][0]) <= 1e-2 * orr["losses"][0]
+    G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
+    for n in G:
+        assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+    assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-2
 
 
 def test_vocab_padding_128_reproduces_65():

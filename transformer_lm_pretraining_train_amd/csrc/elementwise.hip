@@ -276,6 +276,149 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   for (int c = threadIdx.x; c < 3 * C; c += blockDim.x) dst[c] = red[c];
 }
 
+// The same backward for C = 256 NC (the GPT-2 widths): a half-wave (32
+// lanes) per row with NC 8-column chunks per lane, so that every lane is
+// busy and each wave has two rows in flight, and the inputs of a wave's next
+// pair of rows are loaded while the current pair is computed.  The two
+// half-waves of a wave hold the same columns; their column sums are added by
+// one lane exchange, then the four waves' sums in order through LDS.
+template <class T> struct Raw8 {  // 8 elements of T as loaded: 16 or 32 bytes
+  uint4 u[sizeof(T) / 2];
+};
+template <class T> __device__ __forceinline__ void load_raw(const T* p, Raw8<T>& r) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.u[i] = reinterpret_cast<const uint4*>(p)[i];
+}
+__device__ __forceinline__ void unpack8(const Raw8<bf16>& r, float v[8]) {
+  const uint32_t wd[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // element 2k in the low half of word k
+    v[2 * k] = __uint_as_float(wd[k] << 16);
+    v[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float v[8]) {
+  v[0] = __uint_as_float(r.u[0].x); v[1] = __uint_as_float(r.u[0].y);
+  v[2] = __uint_as_float(r.u[0].z); v[3] = __uint_as_float(r.u[0].w);
+  v[4] = __uint_as_float(r.u[1].x); v[5] = __uint_as_float(r.u[1].y);
+  v[6] = __uint_as_float(r.u[1].z); v[7] = __uint_as_float(r.u[1].w);
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <class T, int NC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void layernorm_bwd_hw_kernel(
+    T* __restrict__ dres, float* __restrict__ partial, const T* __restrict__ dy,
+    const T* __restrict__ inp, const float* __restrict__ mean, const float* __restrict__ rstd,
+    const float* __restrict__ w, int M, int C, int accumulate) {
+  static_assert(LNB_ROWS % 8 == 0, "whole rows per half-wave");
+  __shared__ float red[4][3 * 256 * NC];
+  const int wave = threadIdx.x / 64, l = threadIdx.x % 32;
+  const int hw = 2 * wave + (threadIdx.x / 32) % 2;  // half-wave: rows row0 + hw + 8 i
+  float wv[NC][8];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) load8(w + (l + 32 * j) * 8, wv[j]);
+  float dwacc[NC][8], dbacc[NC][8], doacc[NC][8];
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dwacc[j][i] = dbacc[j][i] = doacc[j][i] = 0.f;
+
+  auto fetch = [&](int row, Raw8<T> (&x)[NC], Raw8<T> (&g)[NC], Raw8<T> (&d)[NC]) {
+    if (row < M) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int64_t off = (int64_t)row * C + (l + 32 * j) * 8;
+        load_raw(inp + off, x[j]);
+        load_raw(dy + off, g[j]);
+        if (accumulate) load_raw(dres + off, d[j]);
+      }
+    }
+  };
+  auto process = [&](int row, const Raw8<T> (&x)[NC], const Raw8<T> (&g)[NC],
+                     const Raw8<T> (&d)[NC]) {
+    if (row >= M) return;  // uniform over the half-wave; its sums stay inside it
+    const float mu = mean[row], rs = rstd[row];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      float xv[8], gv[8];
+      unpack8(x[j], xv);
+      unpack8(g[j], gv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xh = (xv[i] - mu) * rs, gw = gv[i] * wv[j][i];
+        s1 += gw;
+        s2 += gw * xh;
+        dwacc[j][i] += gv[i] * xh;
+        dbacc[j][i] += gv[i];
+      }
+    }
+    s1 = half_wave_sum(s1) / C;
+    s2 = half_wave_sum(s2) / C;
+    // second pass over the same registers (x-hat and g*w recomputed, not kept)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      float xv[8], gv[8], dv[8];
+      unpack8(x[j], xv);
+      unpack8(g[j], gv);
+      if (accumulate) unpack8(d[j], dv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xh = (xv[i] - mu) * rs, gw = gv[i] * wv[j][i];
+        const float dx = rs * (gw - s1 - xh * s2);
+        dv[i] = accumulate ? dv[i] + dx : dx;
+        doacc[j][i] += dv[i];
+      }
+      store8(dres + (int64_t)row * C + (l + 32 * j) * 8, dv);
+    }
+  };
+
+  const int r0 = blockIdx.x * LNB_ROWS + hw;
+  constexpr int RPH = LNB_ROWS / 8;  // rows per half-wave
+  Raw8<T> xa[NC], ga[NC], da[NC];
+  fetch(r0, xa, ga, da);
+#pragma unroll 1
+  for (int i = 0; i < RPH; ++i) {
+    Raw8<T> xb[NC], gb[NC], db[NC];
+    if (i + 1 < RPH) fetch(r0 + 8 * (i + 1), xb, gb, db);
+    process(r0 + 8 * i, xa, ga, da);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      xa[j] = xb[j];
+      ga[j] = gb[j];
+      da[j] = db[j];
+    }
+  }
+  // lanes l and l + 32 hold the same columns: add the two half-waves
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dwacc[j][i] += __shfl_xor(dwacc[j][i], 32, 64);
+      dbacc[j][i] += __shfl_xor(dbacc[j][i], 32, 64);
+      doacc[j][i] += __shfl_xor(doacc[j][i], 32, 64);
+    }
+  if (threadIdx.x % 64 < 32) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = (l + 32 * j) * 8 + i;
+        red[wave][c] = dwacc[j][i];
+        red[wave][C + c] = dbacc[j][i];
+        red[wave][2 * C + c] = doacc[j][i];
+      }
+  }
+  __syncthreads();
+  float* dst = partial + (int64_t)blockIdx.x * 3 * C;
+  for (int c = threadIdx.x; c < 3 * C; c += blockDim.x)
+    dst[c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
 // out_k[c] += sum_b partial[b * stride + k * C + c] for each non-null out_k
 // (k = 0, 1, 2), summed in a fixed order.  A workgroup covers 64 columns of
 // the concatenated outputs with 16 float4 lanes x 16 groups of partial rows
@@ -331,11 +474,22 @@ hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, float* d
   DISPATCH_DT(dt, layernorm_bwd_kernel<T, NC><<<nb, 256, lds, s>>>(                            \
                       (T*)dres, partial, (const T*)dy, (const T*)inp, mean, rstd, w, M, C,      \
                       accumulate ? 1 : 0))
-  if (nch == 1) LNB(1);
+#define LNBH(T, NC)                                                                            \
+  layernorm_bwd_hw_kernel<T, NC><<<nb, 256, 0, s>>>((T*)dres, partial, (const T*)dy,           \
+                                                    (const T*)inp, mean, rstd, w, M, C,        \
+                                                    accumulate ? 1 : 0)
+  // the half-wave kernel where its registers suffice: bf16 up to C = 768, fp32 up to 512
+  if (C == 256 && dt == BF16) LNBH(bf16, 1);
+  else if (C == 256) LNBH(float, 1);
+  else if (C == 512 && dt == BF16) LNBH(bf16, 2);
+  else if (C == 512) LNBH(float, 2);
+  else if (C == 768 && dt == BF16) LNBH(bf16, 3);
+  else if (nch == 1) LNB(1);
   else if (nch == 2) LNB(2);
   else if (nch == 3) LNB(3);
   else LNB(4);
 #undef LNB
+#undef LNBH
   const int ncols = dsum ? 3 * C : 2 * C;
   column_partials_reduce_kernel<<<grid_for(ncols, 64), 256, 0, s>>>(dw, db, dsum, partial, nb, C,
                                                                      3 * C, ncols);
