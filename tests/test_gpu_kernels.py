@@ -170,6 +170,58 @@ def test_gemm_weight_gradient_split_k(M, N):
     assert rel_l2(out.cpu().numpy(), ref.cpu().numpy()) < 1e-5
 
 
+def _acc_group_case(dt, shapes, K, seed, ws="auto"):
+    """out_i = init_i + A_i^T B_i through gemm_acc_group; A_i (K, M_i), B_i
+    (K, N_i) row-major, reference in fp64 on the host."""
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dt == BF16 else torch.float32
+    As, Bs, outs, refs = [], [], [], []
+    for M, N in shapes:
+        A = rng.standard_normal((K, M)).astype(np.float32)
+        B = rng.standard_normal((K, N)).astype(np.float32)
+        if dt == BF16:
+            A, B = bf16_round(A), bf16_round(B)
+        init = rng.standard_normal((M, N)).astype(np.float32)
+        As.append(to_dev(A, tdt))
+        Bs.append(to_dev(B, tdt))
+        outs.append(to_dev(init))
+        refs.append(init.astype(np.float64) + A.astype(np.float64).T @ B.astype(np.float64))
+    Ms, Ns = [m for m, _ in shapes], [n for _, n in shapes]
+    nb = g.gemm_acc_group_workspace_bytes(dt, Ms, Ns, K, Ms, Ns)
+    wsb = None
+    if ws == "none":
+        wsb = torch.empty(8, dtype=torch.uint8, device="cuda")
+    print(f"acc group dt={dt} shapes={shapes} K={K} ws={nb} ({ws})", flush=True)
+    g.gemm_acc_group(dt, Ms, Ns, K, As, Ms, Bs, Ns, outs, Ns, ws=wsb)
+    torch.cuda.synchronize()
+    for o, r in zip(outs, refs):
+        assert rel_l2(host(o), r) < 1e-5, (o.shape, rel_l2(host(o), r))
+    return nb
+
+
+def test_weight_gradients_of_a_layer_in_one_launch():
+    """The four weight-gradient products of a 124M layer (fcp, fc, proj, qkv)
+    as one launch, K = 4096 tokens (split in two), full outputs vs fp64."""
+    nb = _acc_group_case(BF16, [(768, 3072), (3072, 768), (768, 768), (2304, 768)], 4096, 11)
+    assert nb == 2 * 4 * (768 * 3072 * 2 + 768 * 768 + 2304 * 768)
+
+
+@pytest.mark.parametrize("K", [1000, 2056])
+def test_weight_gradient_group_ragged(K):
+    """Widths that leave ragged tiles (C = 384) and K with a partial last
+    k-tile; K = 1000 runs unsplit, K = 2056 split in two."""
+    _acc_group_case(BF16, [(384, 1536), (1536, 384), (384, 384), (1152, 384)], K, 12)
+
+
+def test_weight_gradient_group_fallbacks():
+    """Without workspace, with one or three products, and in fp32 (one
+    product per launch) the results are the same products."""
+    _acc_group_case(BF16, [(768, 3072), (2304, 768)], 2048, 13, ws="none")
+    _acc_group_case(BF16, [(512, 256)], 2048, 14)
+    _acc_group_case(BF16, [(256, 128), (512, 512), (304, 136)], 512, 15)
+    _acc_group_case(FP32, [(96, 40), (64, 64)], 200, 16)
+
+
 # ------------------------------------------------------------------ attention
 def attention_case(dt, B, T, H, hd, seed):
     rng = np.random.default_rng(seed)

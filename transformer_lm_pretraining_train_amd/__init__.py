@@ -15,7 +15,8 @@ import os
 
 __all__ = [
     "GPT2Config", "TensorInfo", "GPT2Error", "lib", "library_path", "Model", "param_layout",
-    "num_params", "workspace_bytes", "gemm", "gemm_workspace_bytes", "attention_forward", "attention_backward",
+    "num_params", "workspace_bytes", "gemm", "gemm_workspace_bytes", "gemm_acc_group",
+    "gemm_acc_group_workspace_bytes", "attention_forward", "attention_backward",
     "attention_backward_scratch_bytes", "flops_per_token", "config_for",
     "GPT2_FP32", "GPT2_BF16", "EPI",
 ]
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "gpt2k_gemm": (I, [I, I, I, I, I, I, P, I64, P, I64, I, P, I64, P, P, I64, P, I64, P,
                                I64, P, SZ, P]),
             "gpt2k_gemm_workspace_bytes": (SZ, [I, I, I, I, I]),
+            "gpt2k_gemm_acc_group_workspace_bytes": (SZ, [I, I, P, P, I, P, P]),
+            "gpt2k_gemm_acc_group": (I, [I, I, P, P, I, P, P, P, P, P, P, P, SZ, P]),
             "gpt2k_attention_forward": (I, [I, P, P, P, I, I, I, I, P]),
             "gpt2k_attention_backward_scratch_bytes": (SZ, [I, I, I]),
             "gpt2k_attention_backward": (I, [I, P, P, P, P, P, I, I, I, I, P, P]),
@@ -284,6 +287,39 @@ def gemm(dtype, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, epilogue, out, ldo,
     _check(lib().gpt2k_gemm(dtype, int(a_kmajor), int(b_kmajor), M, N, K, _ptr(A), lda, _ptr(B),
                             ldb, epi, _ptr(out), ldo, _ptr(bias), _ptr(resid), ldr, _ptr(out2),
                             ldo2, _ptr(aux), ldx, _ptr(ws), nbytes, _stream(stream)))
+
+
+def _arr(ctype, vals):
+    a = (ctype * len(vals))(*vals)
+    return a, ctypes.cast(a, ctypes.c_void_p)
+
+
+def gemm_acc_group_workspace_bytes(dtype, Ms, Ns, K, ldas, ldbs):
+    n = len(Ms)
+    keep = [_arr(ctypes.c_int, Ms), _arr(ctypes.c_int, Ns), _arr(ctypes.c_int64, ldas),
+            _arr(ctypes.c_int64, ldbs)]
+    return lib().gpt2k_gemm_acc_group_workspace_bytes(dtype, n, keep[0][1], keep[1][1], K,
+                                                       keep[2][1], keep[3][1])
+
+
+def gemm_acc_group(dtype, Ms, Ns, K, As, ldas, Bs, ldbs, outs, ldos, ws=None, stream=None):
+    """out_i += A_i^T B_i (m-major A_i, n-major B_i) for up to four products
+    sharing K, in one launch where possible (see gpt2_kernels.h).  A split-K
+    workspace is allocated here when ``ws`` is None and one is needed."""
+    n = len(Ms)
+    if ws is None:
+        nb = gemm_acc_group_workspace_bytes(dtype, Ms, Ns, K, ldas, ldbs)
+        if nb:
+            import torch
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    keep = [_arr(ctypes.c_int, Ms), _arr(ctypes.c_int, Ns), _arr(ctypes.c_void_p, [a.data_ptr() for a in As]),
+            _arr(ctypes.c_int64, ldas), _arr(ctypes.c_void_p, [b.data_ptr() for b in Bs]),
+            _arr(ctypes.c_int64, ldbs), _arr(ctypes.c_void_p, [o.data_ptr() for o in outs]),
+            _arr(ctypes.c_int64, ldos)]
+    _check(lib().gpt2k_gemm_acc_group(dtype, n, keep[0][1], keep[1][1], K, keep[2][1], keep[3][1],
+                                      keep[4][1], keep[5][1], keep[6][1], keep[7][1], _ptr(ws),
+                                      nbytes, _stream(stream)))
 
 
 def attention_forward(dtype, out, lse, qkv, B, T, H, hd, stream=None):

@@ -111,6 +111,34 @@ hipError_t encoder_backward_wpe(int dt, float* dwpe, const void* dx, int B, int 
 
 // =========================================================== LayerNorm
 // One wave per row; lane j owns 8-element chunks j, j+64, ... (C % 8 == 0).
+// 8 elements of T as loaded (16 or 32 bytes), unpacked to floats on use.
+template <class T> struct Raw8 {  // 8 elements of T as loaded: 16 or 32 bytes
+  uint4 u[sizeof(T) / 2];
+};
+template <class T> __device__ __forceinline__ void load_raw(const T* p, Raw8<T>& r) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.u[i] = reinterpret_cast<const uint4*>(p)[i];
+}
+__device__ __forceinline__ void unpack8(const Raw8<bf16>& r, float v[8]) {
+  const uint32_t wd[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // element 2k in the low half of word k
+    v[2 * k] = __uint_as_float(wd[k] << 16);
+    v[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float v[8]) {
+  v[0] = __uint_as_float(r.u[0].x); v[1] = __uint_as_float(r.u[0].y);
+  v[2] = __uint_as_float(r.u[0].z); v[3] = __uint_as_float(r.u[0].w);
+  v[4] = __uint_as_float(r.u[1].x); v[5] = __uint_as_float(r.u[1].y);
+  v[6] = __uint_as_float(r.u[1].z); v[7] = __uint_as_float(r.u[1].w);
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 constexpr int LN_MAXCH = 4;  // C <= 8 * 64 * 4 = 2048
 
 template <class T>
@@ -168,10 +196,68 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(
   }
 }
 
+// The same for C = 256 NC: a half-wave (32 lanes) per row, NC 8-column
+// chunks per lane, so that every lane is busy and a wave has two rows in
+// flight.
+template <class T, int NC>
+__global__ __launch_bounds__(256) void layernorm_fwd_hw_kernel(
+    T* __restrict__ out, float* __restrict__ mean_out, float* __restrict__ rstd_out,
+    const T* __restrict__ inp, const float* __restrict__ w, const float* __restrict__ b, int M,
+    int C, float eps) {
+  const int row = blockIdx.x * 8 + threadIdx.x / 32;
+  const int l = threadIdx.x % 32;
+  if (row >= M) return;  // uniform over the half-wave
+  Raw8<T> xr[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) load_raw(inp + (int64_t)row * C + (l + 32 * j) * 8, xr[j]);
+  float v[NC][8];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    unpack8(xr[j], v[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[j][i];
+  }
+  const float mean = half_wave_sum(s) / C;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = v[j][i] - mean;
+      ss += d * d;
+    }
+  const float rstd = 1.0f / sqrtf(half_wave_sum(ss) / C + eps);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int c = (l + 32 * j) * 8;
+    float wv[8], bv[8], o[8];
+    load8(w + c, wv);
+    load8(b + c, bv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (v[j][i] - mean) * rstd * wv[i] + bv[i];
+    store8(out + (int64_t)row * C + c, o);
+  }
+  if (l == 0) {
+    mean_out[row] = mean;
+    rstd_out[row] = rstd;
+  }
+}
+
 hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,
                              const float* w, const float* b, int M, int C, float eps,
                              hipStream_t s) {
   if (C % 8 != 0 || C > 8 * 64 * LN_MAXCH) return hipErrorInvalidValue;
+  if (C == 256 || C == 512 || C == 768) {
+#define LNFH(NC)                                                                               \
+  DISPATCH_DT(dt, layernorm_fwd_hw_kernel<T, NC><<<grid_for(M, 8), 256, 0, s>>>(               \
+                      (T*)out, mean, rstd, (const T*)inp, w, b, M, C, eps))
+    if (C == 256) LNFH(1);
+    else if (C == 512) LNFH(2);
+    else LNFH(3);
+#undef LNFH
+    return hipGetLastError();
+  }
   DISPATCH_DT(dt, layernorm_fwd_kernel<T><<<grid_for(M, 4), 256, 0, s>>>(
                       (T*)out, mean, rstd, (const T*)inp, w, b, M, C, eps));
   return hipGetLastError();
@@ -179,9 +265,10 @@ hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const 
 
 // Backward: per row, g = dy * w, xhat = (x - mean) rstd,
 // dx = rstd (g - mean(g) - xhat mean(g xhat)); dres = dx (first) or
-// dres += dx.  Each workgroup handles LNB_ROWS rows and writes partial
-// column sums of dy*xhat, of dy and of the new dres (the bias gradient of
-// the linear layer whose output is that residual) to
+// dres = dres_in + dx (dres_in may be dres itself).  Each workgroup handles
+// LNB_ROWS rows and writes partial column sums of dy*xhat, of dy and of the
+// new dres (the bias gradient of the linear layer whose output is that
+// residual) to
 // scratch[block][3][C]; column_partials_reduce adds them up.  NCH: 8-column
 // chunks per lane (C <= 512 NCH), so that no registers are spent on
 // columns that do not exist.
@@ -189,7 +276,7 @@ constexpr int LNB_ROWS = 32;
 
 template <class T, int NCH>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
-    T* __restrict__ dres, float* __restrict__ partial, const T* __restrict__ dy,
+    T* dres, const T* dres_in, float* __restrict__ partial, const T* __restrict__ dy,
     const T* __restrict__ inp, const float* __restrict__ mean, const float* __restrict__ rstd,
     const float* __restrict__ w, int M, int C, int accumulate) {
   extern __shared__ float red[];  // [3][C]
@@ -209,6 +296,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     const T* x = inp + (int64_t)row * C;
     const T* g = dy + (int64_t)row * C;
     T* d = dres + (int64_t)row * C;
+    const T* din = dres_in + (int64_t)row * C;
     float xh[NCH][8], gw[NCH][8], dv[NCH][8];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -219,7 +307,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
         load8(x + ch * 8, xv);
         load8(g + ch * 8, gv);
         load8(w + ch * 8, wv);
-        if (accumulate) load8(d + ch * 8, dv[j]);
+        if (accumulate) load8(din + ch * 8, dv[j]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           xh[j][i] = (xv[i] - mu) * rs;
@@ -282,36 +370,9 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
 // pair of rows are loaded while the current pair is computed.  The two
 // half-waves of a wave hold the same columns; their column sums are added by
 // one lane exchange, then the four waves' sums in order through LDS.
-template <class T> struct Raw8 {  // 8 elements of T as loaded: 16 or 32 bytes
-  uint4 u[sizeof(T) / 2];
-};
-template <class T> __device__ __forceinline__ void load_raw(const T* p, Raw8<T>& r) {
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.u[i] = reinterpret_cast<const uint4*>(p)[i];
-}
-__device__ __forceinline__ void unpack8(const Raw8<bf16>& r, float v[8]) {
-  const uint32_t wd[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {  // element 2k in the low half of word k
-    v[2 * k] = __uint_as_float(wd[k] << 16);
-    v[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void unpack8(const Raw8<float>& r, float v[8]) {
-  v[0] = __uint_as_float(r.u[0].x); v[1] = __uint_as_float(r.u[0].y);
-  v[2] = __uint_as_float(r.u[0].z); v[3] = __uint_as_float(r.u[0].w);
-  v[4] = __uint_as_float(r.u[1].x); v[5] = __uint_as_float(r.u[1].y);
-  v[6] = __uint_as_float(r.u[1].z); v[7] = __uint_as_float(r.u[1].w);
-}
-__device__ __forceinline__ float half_wave_sum(float v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 template <class T, int NC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void layernorm_bwd_hw_kernel(
-    T* __restrict__ dres, float* __restrict__ partial, const T* __restrict__ dy,
+    T* dres, const T* dres_in, float* __restrict__ partial, const T* __restrict__ dy,
     const T* __restrict__ inp, const float* __restrict__ mean, const float* __restrict__ rstd,
     const float* __restrict__ w, int M, int C, int accumulate) {
   static_assert(LNB_ROWS % 8 == 0, "whole rows per half-wave");
@@ -334,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t off = (int64_t)row * C + (l + 32 * j) * 8;
         load_raw(inp + off, x[j]);
         load_raw(dy + off, g[j]);
-        if (accumulate) load_raw(dres + off, d[j]);
+        if (accumulate) load_raw(dres_in + off, d[j]);
       }
     }
   };
@@ -461,8 +522,9 @@ size_t layernorm_backward_scratch_bytes(int M, int C) {
   return (size_t)cdiv(M, LNB_ROWS) * 3 * C * sizeof(float);
 }
 
-hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, float* dsum,
-                              bool accumulate, const void* dy, const void* inp, const float* mean,
+hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw, float* db,
+                              float* dsum, bool accumulate, const void* dy, const void* inp,
+                              const float* mean,
                               const float* rstd, const float* w, int M, int C, void* scratch,
                               hipStream_t s) {
   if (C % 8 != 0 || C > 8 * 64 * LN_MAXCH) return hipErrorInvalidValue;
@@ -472,12 +534,12 @@ hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, float* d
   const size_t lds = 3 * C * sizeof(float);
 #define LNB(NC)                                                                                \
   DISPATCH_DT(dt, layernorm_bwd_kernel<T, NC><<<nb, 256, lds, s>>>(                            \
-                      (T*)dres, partial, (const T*)dy, (const T*)inp, mean, rstd, w, M, C,      \
-                      accumulate ? 1 : 0))
+                      (T*)dres, (const T*)(dres_in ? dres_in : dres), partial, (const T*)dy,    \
+                      (const T*)inp, mean, rstd, w, M, C, accumulate ? 1 : 0))
 #define LNBH(T, NC)                                                                            \
-  layernorm_bwd_hw_kernel<T, NC><<<nb, 256, 0, s>>>((T*)dres, partial, (const T*)dy,           \
-                                                    (const T*)inp, mean, rstd, w, M, C,        \
-                                                    accumulate ? 1 : 0)
+  layernorm_bwd_hw_kernel<T, NC><<<nb, 256, 0, s>>>(                                           \
+      (T*)dres, (const T*)(dres_in ? dres_in : dres), partial, (const T*)dy, (const T*)inp, mean, \
+      rstd, w, M, C, accumulate ? 1 : 0)
   // the half-wave kernel where its registers suffice: bf16 up to C = 768, fp32 up to 512
   if (C == 256 && dt == BF16) LNBH(bf16, 1);
   else if (C == 256) LNBH(float, 1);

@@ -477,12 +477,49 @@ struct BigSmem {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// One product of a launch.  Up to kMaxGroup products with the same K and
+// operand orientations share a launch, gridDim.z selecting the product
+// (the weight gradients of one layer run as one launch this way).
+struct BigProblem {
+  int M, N, tiles_m, tiles_n;
+  const bf16* A;
+  int64_t lda;
+  const bf16* B;
+  int64_t ldb;
+  Epilogue e;
+};
+constexpr int kMaxGroup = 4;
+struct BigBatch {
+  BigProblem p[kMaxGroup];
+  // Grouped launches (grouped != 0): a 1-D grid of work items, product i owning
+  // items item0[i] .. item0[i+1]-1 = its tiles x `splits` K ranges, one
+  // tile per workgroup.  Items are numbered product-major, then split,
+  // then tile (in tile_of order), and dealt to the XCDs in contiguous
+  // ranges, so that the workgroups of an XCD cover compact blocks of tiles
+  // of one product and share its operand panels in their L2.
+  int grouped, n, splits;
+  int item0[kMaxGroup + 1];
+};
+
 template <int BM, int BN, bool AKM, bool BKM, int MODE>
-__global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, int N, int K,
-                                                               const bf16* __restrict__ A, int64_t lda,
-                                                               const bf16* __restrict__ B, int64_t ldb,
-                                                               Epilogue e, int kps, int tiles_m,
-                                                               int tiles_n) {
+__global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const BigBatch batch,
+                                                                         int K, int kps) {
+  int prob = 0, split = blockIdx.y, first = xcd_remap(blockIdx.x, gridDim.x), step = gridDim.x;
+  if (batch.grouped) {
+    const int item = first;
+    while (prob + 1 < batch.n && item >= batch.item0[prob + 1]) ++prob;
+    const int r = item - batch.item0[prob];
+    const int nt = batch.p[prob].tiles_m * batch.p[prob].tiles_n;
+    split = r / nt;
+    first = r % nt;
+    step = nt;  // this tile only
+  }
+  const BigProblem& P = batch.p[prob];
+  const int M = P.M, N = P.N, tiles_m = P.tiles_m, tiles_n = P.tiles_n;
+  const bf16* __restrict__ A = P.A;
+  const bf16* __restrict__ B = P.B;
+  const int64_t lda = P.lda, ldb = P.ldb;
+  const Epilogue& e = P.e;
   using SM = BigSmem<BM, BN, AKM, BKM>;
   using OA = typename SM::OA;
   using OB = typename SM::OB;
@@ -499,11 +536,11 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
   // workgroups, at most one per CU), with w numbered XCD-major so that the
   // tiles an XCD works on at the same time are neighbours and share its L2.
   const int ntiles = tiles_m * tiles_n;
-  for (int tile = xcd_remap(blockIdx.x, gridDim.x); tile < ntiles; tile += gridDim.x) {
+  for (int tile = first; tile < ntiles; tile += step) {
   int tm, tn;
   tile_of(tile, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kbeg = blockIdx.y * kps;
+  const int kbeg = split * kps;
   const int kend = min(K, kbeg + kps);
   const int nk = kend > kbeg ? (int)cdiv(kend - kbeg, 64) : 0;
 
@@ -622,7 +659,7 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(int M, 
         const float4 b = *reinterpret_cast<const float4*>(slab + row * SP + col + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const int m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + jr * JB * 32 + col;
-        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, blockIdx.y, M);
+        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, split, M);
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -706,7 +743,12 @@ hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, in
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
   const int g = (int)(splits > 1 ? ntiles : (ntiles < kCUs ? ntiles : kCUs));
   dim3 grid((unsigned)g, (unsigned)splits);
-#define GO(AK, BK_) gemm_big_kernel<BM, BN, AK, BK_, MODE><<<grid, BigWaves<BN>::NW * 64, 0, s>>>(M, N, K, a, lda, b, ldb, e, kps, tiles_m, tiles_n)
+  BigBatch batch{};
+  batch.p[0] = BigProblem{M, N, tiles_m, tiles_n, a, lda, b, ldb, e};
+  batch.grouped = 0;
+  batch.n = 1;
+  batch.splits = splits;
+#define GO(AK, BK_) gemm_big_kernel<BM, BN, AK, BK_, MODE><<<grid, BigWaves<BN>::NW * 64, 0, s>>>(batch, K, kps)
   if (akm && bkm) GO(true, true);
   else if (akm && !bkm) GO(true, false);
   else if (!akm && !bkm) GO(false, false);
@@ -784,6 +826,103 @@ int acc_row_split(int dt, int M, int N, int K, int mode) {
   if (full == 0 || rest == 0 || rest * 2 > kCUs) return 0;
   const int64_t rows = full / tn * 256;
   return rows > 0 && rows < M ? (int)rows : 0;
+}
+
+// ---------------------------------------------------------------- grouped weight gradients
+// out_i (fp32) += A_i^T B_i for up to kMaxGroup products that share K (the
+// token count): A_i[k * lda + m] (m < M_i), B_i[k * ldb + n] (n < N_i).  The
+// four weight gradients of a layer have 9-36 output tiles each, far fewer
+// than the CUs; run as one launch, their tiles together fill the chip with
+// a split of K into S parts (S from the total tile count), so that the
+// partial tiles cost S x (sum of M_i N_i) floats instead of each product's
+// own, larger split.  Returns 0 where the grouped launch does not apply.
+static int acc_group_splits(int dt, int n, const AccItem* it, int K) {
+  if (dt != BF16 || n < 1 || n > kMaxGroup || K % 8 != 0 || K <= 0) return 0;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (it[i].M < 256 || it[i].N < 128 || it[i].lda % 8 || it[i].ldb % 8) return 0;
+    if (operand_span(false, it[i].M, K, it[i].lda) >= (int64_t(1) << 31) ||
+        operand_span(false, it[i].N, K, it[i].ldb) >= (int64_t(1) << 31))
+      return 0;
+    total += cdiv(it[i].M, 256) * cdiv(it[i].N, 256);
+  }
+  if (total > kCUs) return 0;
+  int S = (int)(kCUs / total);
+  S = std::min(S, 16);
+  S = std::min(S, std::max(1, K / 1024));
+  return std::max(S, 1);
+}
+
+size_t gemm_acc_group_workspace_bytes(int dt, int n, const AccItem* it, int K) {
+  const int S = acc_group_splits(dt, n, it, K);
+  if (S <= 1) return 0;
+  size_t t = 0;
+  for (int i = 0; i < n; ++i) t += round_up((int64_t)it[i].M * it[i].N, 64) * sizeof(float);
+  return t * S;
+}
+
+hipError_t gemm_acc_group(int dt, int n, const AccItem* it, int K, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
+  int S = acc_group_splits(dt, n, it, K);
+  bool vec4 = true;
+  for (int i = 0; i < n; ++i) vec4 = vec4 && it[i].N % 4 == 0 && it[i].ldo % 4 == 0;
+  if (S > 1 && (!ws || ws_bytes < gemm_acc_group_workspace_bytes(dt, n, it, K) || !vec4)) S = 0;
+  if (S == 0) {  // one launch per product
+    for (int i = 0; i < n; ++i) {
+      Epilogue e{};
+      e.mode = EPI_ACC_F32;
+      e.out = it[i].out;
+      e.ldo = it[i].ldo;
+      hipError_t err = gemm(dt, false, false, it[i].M, it[i].N, K, it[i].A, it[i].lda, it[i].B,
+                            it[i].ldb, e, s, ws, ws_bytes);
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+  }
+  BigBatch batch{};
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    BigProblem& p = batch.p[i];
+    p.M = it[i].M;
+    p.N = it[i].N;
+    p.tiles_m = (int)cdiv(p.M, 256);
+    p.tiles_n = (int)cdiv(p.N, 256);
+    p.A = (const bf16*)it[i].A;
+    p.lda = it[i].lda;
+    p.B = (const bf16*)it[i].B;
+    p.ldb = it[i].ldb;
+    p.e = Epilogue{};
+    if (S > 1) {
+      p.e.mode = EPI_PARTIAL;
+      p.e.out = (char*)ws + off;
+      off += round_up((int64_t)p.M * p.N, 64) * sizeof(float) * S;
+    } else {
+      p.e.mode = EPI_ACC_F32;
+      p.e.out = it[i].out;
+      p.e.ldo = it[i].ldo;
+    }
+    batch.item0[i + 1] = batch.item0[i] + p.tiles_m * p.tiles_n * S;
+  }
+  batch.grouped = 1;
+  batch.n = n;
+  batch.splits = S;
+  const int kps = (int)round_up(cdiv(K, S), 64);
+  dim3 grid((unsigned)batch.item0[n]);
+  if (S > 1)
+    gemm_big_kernel<256, 256, false, false, EPI_PARTIAL><<<grid, 512, 0, s>>>(batch, K, kps);
+  else
+    gemm_big_kernel<256, 256, false, false, EPI_ACC_F32><<<grid, 512, 0, s>>>(batch, K, kps);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || S == 1) return err;
+  for (int i = 0; i < n; ++i) {
+    const BigProblem& p = batch.p[i];
+    const int64_t n4 = (int64_t)p.M * p.N / 4;
+    splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, s>>>(
+        it[i].out, it[i].ldo, (const float*)p.e.out, S, p.M, p.N);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode) {

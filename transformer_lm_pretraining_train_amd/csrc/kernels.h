@@ -26,14 +26,15 @@ hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32
 // ---- LayerNorm
 hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,
                              const float* w, const float* b, int M, int C, float eps, hipStream_t s);
-// dres = dx (accumulate false) or dres += dx; dw, db += column sums of
-// dy*xhat and dy; dsum (if not null) += column sums of the new dres.
-// Two-stage, partials in scratch.
+// dres = dx (accumulate false) or dres = dres_in + dx (dres_in null or
+// equal to dres: in place); dw, db += column sums of dy*xhat and dy; dsum
+// (if not null) += column sums of the new dres.  Two-stage, partials in
+// scratch.
 size_t layernorm_backward_scratch_bytes(int M, int C);
-hipError_t layernorm_backward(int dt, void* dres, float* dw, float* db, float* dsum,
-                              bool accumulate, const void* dy, const void* inp, const float* mean,
-                              const float* rstd, const float* w, int M, int C, void* scratch,
-                              hipStream_t s);
+hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw, float* db,
+                              float* dsum, bool accumulate, const void* dy, const void* inp,
+                              const float* mean, const float* rstd, const float* w, int M, int C,
+                              void* scratch, hipStream_t s);
 
 // ---- bias gradient: db[n] += sum_m dy[m, n] (two-stage, partials in scratch)
 size_t bias_grad_scratch_bytes(int M, int N);
@@ -90,6 +91,22 @@ size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode);
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
                 void* ws = nullptr, size_t ws_bytes = 0);
+// out (fp32, pitch ldo) += sum_k A[k * lda + m] B[k * ldb + n] for m < M,
+// n < N: a weight gradient dW += dy^T x with dy and x stored row-major.
+struct AccItem {
+  int M, N;
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  float* out;
+  int64_t ldo;
+};
+// Up to four such products with a common K in one launch (bf16), else one
+// gemm() each; split-K partials need gemm_acc_group_workspace_bytes() in ws.
+size_t gemm_acc_group_workspace_bytes(int dt, int n, const AccItem* items, int K);
+hipError_t gemm_acc_group(int dt, int n, const AccItem* items, int K, void* ws, size_t ws_bytes,
+                          hipStream_t s);
 
 // ---- optimizer
 struct DecayMap {  // which flat elements belong to 2-D tensors

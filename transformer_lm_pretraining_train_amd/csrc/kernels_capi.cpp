@@ -57,6 +57,43 @@ size_t gpt2k_gemm_workspace_bytes(int dtype, int M, int N, int K, int epilogue) 
   return gemm_workspace_bytes(dtype, M, N, K, epilogue);
 }
 
+static bool acc_items(int n, const int* M, const int* N, const int64_t* lda, const int64_t* ldb,
+                      AccItem* it) {
+  if (n < 1 || n > 4 || !M || !N || !lda || !ldb) return false;
+  for (int i = 0; i < n; ++i) {
+    if (M[i] < 0 || N[i] < 0 || lda[i] % 8 || ldb[i] % 8) return false;
+    it[i] = AccItem{M[i], N[i], nullptr, lda[i], nullptr, ldb[i], nullptr, 0};
+  }
+  return true;
+}
+
+size_t gpt2k_gemm_acc_group_workspace_bytes(int dtype, int n, const int* M, const int* N, int K,
+                                            const int64_t* lda, const int64_t* ldb) {
+  AccItem it[4];
+  if (!acc_items(n, M, N, lda, ldb, it) || K < 0) return 0;
+  return gemm_acc_group_workspace_bytes(dtype, n, it, K);
+}
+
+int gpt2k_gemm_acc_group(int dtype, int n, const int* M, const int* N, int K, const void* const* A,
+                         const int64_t* lda, const void* const* B, const int64_t* ldb,
+                         float* const* out, const int64_t* ldo, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
+    return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
+  AccItem it[4];
+  if (!acc_items(n, M, N, lda, ldb, it) || K < 0 || !A || !B || !out || !ldo)
+    return gpt2_internal_fail(GPT2_EINVAL, "bad group: n, sizes, pitches or NULL arrays");
+  for (int i = 0; i < n; ++i) {
+    if (!A[i] || !B[i] || !out[i]) return gpt2_internal_fail(GPT2_EINVAL, "NULL operand");
+    it[i].A = A[i];
+    it[i].B = B[i];
+    it[i].out = out[i];
+    it[i].ldo = ldo[i];
+  }
+  return launch_rc(gemm_acc_group(dtype, n, it, K, ws, ws_bytes, (hipStream_t)stream),
+                   "gemm_acc_group");
+}
+
 int gpt2k_attention_forward(int dtype, void* out, float* lse, const void* qkv, int B, int T, int H,
                             int hd, void* stream) {
   if (dtype != GPT2_FP32 && dtype != GPT2_BF16)

@@ -7,11 +7,13 @@
 // AdamW m and v; the bf16 copy of the parameters (bf16 mode); activations
 // kept for the backward; backward buffers; reduction scratch; flags.  The
 // library allocates nothing on the device after gpt2_create.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/gpt2.h"
@@ -150,7 +152,7 @@ struct gpt2_model {
   float *losses, *ce_lse, *loss_internal;
   int32_t* argmax;
   // backward
-  void *dres, *dbuf_c, *dbuf_4c, *dqkv;
+  void *dres, *dres2, *dbuf_c, *dbuf_4c, *dqkv;  // dres, dres2: residual gradient, ping-pong
   void* scratch;
   void* gemm_ws;  // split-K partial tiles of the weight-gradient GEMMs
   size_t gemm_ws_bytes;
@@ -228,6 +230,7 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.argmax = (int32_t*)cv.take(M * 4);
   md.loss_internal = (float*)cv.take(4);
   md.dres = cv.take(M * C * es);
+  md.dres2 = cv.take(M * C * es);
   md.dbuf_c = cv.take(M * C * es);
   md.dbuf_4c = cv.take(M * 4 * C * es);
   md.dqkv = cv.take(M * 3 * C * es);
@@ -242,6 +245,12 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
     const int dWshapes[5][2] = {{c.padded_vocab_size, Ci}, {Ci, 4 * Ci}, {4 * Ci, Ci}, {Ci, Ci},
                                 {3 * Ci, Ci}};
     for (auto& sh : dWshapes) gw = std::max(gw, gemm_workspace_bytes(dt, sh[0], sh[1], Mi, EPI_ACC_F32));
+    // the four weight gradients of a layer as one launch (shapes and pitches only)
+    const AccItem grp[4] = {{Ci, 4 * Ci, nullptr, Ci, nullptr, 4 * Ci, nullptr, 4 * Ci},
+                            {4 * Ci, Ci, nullptr, 4 * Ci, nullptr, Ci, nullptr, Ci},
+                            {Ci, Ci, nullptr, Ci, nullptr, Ci, nullptr, Ci},
+                            {3 * Ci, Ci, nullptr, 3 * Ci, nullptr, Ci, nullptr, Ci}};
+    gw = std::max(gw, gemm_acc_group_workspace_bytes(dt, 4, grp, Mi));
   }
   md.gemm_ws = gw ? cv.take(gw) : nullptr;
   md.gemm_ws_bytes = gw;
@@ -533,49 +542,57 @@ int gpt2_backward(gpt2_model* md) {
   // are the bias gradient of the linear layer that wrote that residual:
   // fc-proj of the layer below (res3) or proj of the same layer (res2).
   float* fcp_b_below = md->L > 0 ? G + Ly.layers[md->L - 1].fcp_b : nullptr;
-  LAUNCH(layernorm_backward(dt, md->dres, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
+  // The residual gradient alternates between two buffers: each layer reads
+  // d res3 from `cur` and leaves d x in `nxt`, so that d res3 is still there
+  // when the layer's weight gradients run together at its end.
+  void* cur = md->dres;
+  void* nxt = md->dres2;
+  LAUNCH(layernorm_backward(dt, cur, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
                             md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
                             md->scratch, s));
   for (int l = md->L - 1; l >= 0; --l) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
     const void* xin = l > 0 ? md->act[l - 1].res3 : md->encoded;
-    // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
-    LAUNCH(gemm(dt, false, false, C, 4 * C, M, md->dres, C, a.fchg, 4 * C,
-                epi(EPI_ACC_F32, G + o.fcp_w, 4 * C), s, md->gemm_ws, md->gemm_ws_bytes));
+    // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b; cur = d res3
     Epilogue e = epi(EPI_GELU_BWD, md->dbuf_4c, 4 * C);
     e.aux = a.fch;
     e.ldx = 4 * C;
-    LAUNCH(gemm(dt, true, false, M, 4 * C, C, md->dres, C, md->wt(o.fcp_w), 4 * C, e, s));
-    // fc: fch = ln2 fc_w^T + fc_b  (dbuf_4c now holds d fch)
-    LAUNCH(gemm(dt, false, false, 4 * C, C, M, md->dbuf_4c, 4 * C, a.ln2, C,
-                epi(EPI_ACC_F32, G + o.fc_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
-    LAUNCH(bias_grad(dt, G + o.fc_b, md->dbuf_4c, M, 4 * C, 4 * C, md->scratch, s));
+    LAUNCH(gemm(dt, true, false, M, 4 * C, C, cur, C, md->wt(o.fcp_w), 4 * C, e, s));
+    // fc: fch = ln2 fc_w^T + fc_b  (dbuf_4c now holds d fch; its column sums
+    // are taken right after the product that reads it)
     LAUNCH(gemm(dt, true, false, M, C, 4 * C, md->dbuf_4c, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
+    LAUNCH(bias_grad(dt, G + o.fc_b, md->dbuf_4c, M, 4 * C, 4 * C, md->scratch, s));
+    // nxt = d res2 = d res3 + the LayerNorm-2 backward
+    LAUNCH(layernorm_backward(dt, nxt, cur, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
                               md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
                               md->scratch, s));
     // attention output projection: res2 = x + atty proj_w^T + proj_b
-    LAUNCH(gemm(dt, false, false, C, C, M, md->dres, C, a.atty, C,
-                epi(EPI_ACC_F32, G + o.proj_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
-    LAUNCH(gemm(dt, true, false, M, C, C, md->dres, C, md->wt(o.proj_w), C,
+    LAUNCH(gemm(dt, true, false, M, C, C, nxt, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
     TIMED(GPT2_TIMER_ATTN_BWD, attention_backward(dt, md->dqkv, md->dbuf_c, a.qkv, a.atty, a.lse,
                                                   md->B, md->Tn, H, md->hd, md->scratch, s));
     // qkv = ln1 qkv_w^T + qkv_b
-    LAUNCH(gemm(dt, false, false, 3 * C, C, M, md->dqkv, 3 * C, a.ln1, C,
-                epi(EPI_ACC_F32, G + o.qkv_w, C), s, md->gemm_ws, md->gemm_ws_bytes));
-    LAUNCH(bias_grad(dt, G + o.qkv_b, md->dqkv, M, 3 * C, 3 * C, md->scratch, s));
     LAUNCH(gemm(dt, true, false, M, C, 3 * C, md->dqkv, 3 * C, md->wt(o.qkv_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(layernorm_backward(dt, md->dres, G + o.ln1_w, G + o.ln1_b,
+    LAUNCH(bias_grad(dt, G + o.qkv_b, md->dqkv, M, 3 * C, 3 * C, md->scratch, s));
+    // the layer's weight gradients dW += dy^T x, as one launch
+    const AccItem dw[4] = {
+        {C, 4 * C, cur, C, a.fchg, 4 * C, G + o.fcp_w, 4 * C},
+        {4 * C, C, md->dbuf_4c, 4 * C, a.ln2, C, G + o.fc_w, C},
+        {C, C, nxt, C, a.atty, C, G + o.proj_w, C},
+        {3 * C, C, md->dqkv, 3 * C, a.ln1, C, G + o.qkv_w, C}};
+    LAUNCH(gemm_acc_group(dt, 4, dw, M, md->gemm_ws, md->gemm_ws_bytes, s));
+    // nxt = d x = d res2 + the LayerNorm-1 backward
+    LAUNCH(layernorm_backward(dt, nxt, nxt, G + o.ln1_w, G + o.ln1_b,
                               l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c, xin,
                               a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, md->scratch, s));
+    std::swap(cur, nxt);
   }
   // embeddings
-  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
-  LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, md->dres, md->B, md->Tn, C, s));
+  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, cur, md->tokens, M, C, md->V, md->scratch, s));
+  LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, cur, md->B, md->Tn, C, s));
   return GPT2_OK;
 }
 
