@@ -112,6 +112,41 @@ def test_gemm_epilogues(dt, epi):
         assert rel_l2(r["got2"], r["expect2"]) < (1e-5 if dt == FP32 else 4e-3)
 
 
+@pytest.mark.parametrize("akm,bkm", ORIENT)
+@pytest.mark.parametrize("K,pad", [(200, 0), (40, 0), (136, 3)])
+def test_gemm_store_persistent_256_tiles(akm, bkm, K, pad):
+    """Products large enough for the persistent 256 x 256 store kernel (4
+    rounds of tiles), ragged in M, N and K, one k-tile (K = 40), and an output
+    pitch that is not a multiple of 8 (every store element-wise); 80 sampled
+    rows, all columns, against fp64."""
+    M, N = 8092, 8132
+    ldo = N + pad
+    print(f"gemm 256x256 store akm={akm} bkm={bkm} M={M} N={N} K={K} ldo={ldo}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(K + pad)
+    kp = (K + 7) // 8 * 8
+    A = torch.randn((M, kp) if akm else (K, M + 4), device="cuda", generator=gen).to(torch.bfloat16)
+    B = torch.randn((N, kp) if bkm else (K, N + 4), device="cuda", generator=gen).to(torch.bfloat16)
+    if akm:
+        A[:, K:] = float("nan")  # the k tail past K must not reach the output
+    if bkm:
+        B[:, K:] = float("nan")
+    out = torch.full((M, ldo), float("nan"), dtype=torch.bfloat16, device="cuda")
+    g.gemm(BF16, akm, bkm, M, N, K, A, A.shape[1], B, B.shape[1], "store", out, ldo)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(K).choice(M, 64, replace=False)
+    extra = [0, 255, 256, M // 2, 7935, 7936, M - 1]  # first, tile borders, last (ragged) tile
+    rows = np.unique(np.concatenate([rows, np.array(extra)]))
+    ridx = torch.from_numpy(rows).cuda()
+    Am = (A[ridx, :K] if akm else A[:, ridx].T).float().cpu().numpy().astype(np.float64)
+    Bm = (B[:, :K] if bkm else B[:, :N].T).float().cpu().numpy().astype(np.float64)
+    ref = Am @ Bm.T
+    got = out[ridx].float().cpu().numpy()
+    assert np.all(np.isfinite(got[:, :N]))
+    assert rel_l2(got[:, :N], ref) < 4e-3
+    if pad:
+        assert np.all(np.isnan(got[:, N:]))  # the pitch padding is not written
+
+
 @pytest.mark.parametrize("akm,bkm,M,N,K", [
     (True, True, 16384, 2304, 768),     # qkv forward
     (True, True, 16384, 3072, 768),     # fc forward
