@@ -80,14 +80,15 @@ def lm_head_roofline(cfg, n, total_ms):
 def other_kernels(cfg, n_timed):
     """Algorithmic work per launch of the other timed steps: causal attention
     (4 hd flops per query-key pair forward, 10 hd backward), the fused
-    cross-entropy forward (one bf16 read of each logit row) and AdamW (30
-    bytes per parameter: read p, g, m, v, write p, m, v and the bf16 copy)."""
+    cross-entropy of the forward (one bf16 read of each logit row and one bf16
+    write of its gradient) and AdamW (30 bytes per parameter: read p, g, m, v,
+    write p, m, v and the bf16 copy)."""
     import transformer_lm_pretraining_train_amd as g
     B, T, H, C = cfg.micro_batch, cfg.seq_len, cfg.n_head, cfg.n_embd
     hd = C // H
     pairs = B * H * T * (T + 1) // 2
     work = {"attn_fwd": (4.0 * hd * pairs, "mfma"), "attn_bwd": (10.0 * hd * pairs, "mfma"),
-            "ce_fwd": (2.0 * B * T * cfg.padded_vocab_size, "hbm"),
+            "ce_fwd": (4.0 * B * T * cfg.padded_vocab_size, "hbm"),
             "adamw": (30.0 * g.num_params(cfg), "hbm")}
     out = {}
     for name, (n, ms) in n_timed.items():

@@ -135,7 +135,9 @@ int gpt2_forward(gpt2_model* model, const int32_t* dev_tokens, const int32_t* de
                  float* dev_loss);
 
 /* Backward pass of the last forward (which must have had targets):
- * gradients += d(mean loss / k) / d params.  Overwrites the logits buffer. */
+ * gradients += d(mean loss / k) / d params.  The logit gradient comes from
+ * the forward's cross-entropy (computed with the loss, from the same read of
+ * the logits); the logits themselves are left as the forward wrote them. */
 int gpt2_backward(gpt2_model* model);
 
 /* Gradients = 0. */
@@ -184,7 +186,8 @@ int gpt2_debug_read(gpt2_model* model, int which, int layer, void* dev_dst, size
  *   LM_HEAD_FWD  the tied-head logits GEMM of each forward
  *   ATTN_FWD     causal attention forward, one pair per layer
  *   ATTN_BWD     attention backward (both of its kernels), one pair per layer
- *   CE_FWD       the fused softmax cross-entropy forward of each forward
+ *   CE_FWD       the fused softmax cross-entropy of each forward with targets
+ *                (loss, lse, argmax and the logit gradient)
  *   ADAMW        the AdamW update of each optimizer step (not the norm) */
 enum {
   GPT2_TIMER_NONE = 0,

@@ -218,6 +218,30 @@ def test_bf16_width_768_matches_oracle():
     assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-2
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_gpt2_vocabulary_matches_oracle(dtype):
+    """The GPT-2 vocabulary (50257 ids padded to 50304) on a one-layer
+    model: the cross-entropy's wide-row paths (bf16: the whole row in the
+    registers of one workgroup; fp32: a loss pass and a gradient pass)."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", dtype, B=2, n_layer=1,
+                                                      vocab_size=50257, padded_vocab_size=50304)
+    print(f"{dtype} V=50257 Vp=50304", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
+    if dtype == "fp32":
+        assert abs(gs[0]["losses"][0] - orr["losses"][0]) <= 1e-4 * orr["losses"][0]
+        for n in G:
+            assert rel_l2(G[n], O[n]) <= 1e-3, (n, rel_l2(G[n], O[n]))
+    else:
+        assert abs(gs[0]["losses"][0] - orr["losses"][0]) <= 1e-2 * orr["losses"][0]
+        for n in G:
+            assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+    # padded vocabulary rows of the tied embedding get no gradient
+    wte = G["wte"].reshape(50304, -1)
+    assert np.all(wte[50257:] == 0)
+
+
 def test_vocab_padding_128_reproduces_65():
     """Padding the 65-id vocabulary to 128 gives the same loss and the same
     gradients on rows < 65; padded rows keep zero gradient and stay zero."""

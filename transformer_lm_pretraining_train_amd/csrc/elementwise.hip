@@ -712,18 +712,20 @@ hipError_t mean_loss(float* out, const float* losses, int M, hipStream_t s) {
   return hipGetLastError();
 }
 
-// dz = seed * (exp(z - lse) - [c == y]) for c < V, 0 for V <= c < ldl.
+// dz = seed * (exp(z - lse) - [c == y]) for c < V, 0 for V <= c < ldl
+// (rows too wide for the fused kernel below).
 template <class T>
-__global__ void ce_bwd_kernel(T* __restrict__ logits, int64_t ldl, const float* __restrict__ lse,
-                              const int32_t* __restrict__ targets, int M, int V, float seed) {
+__global__ void ce_bwd_kernel(T* __restrict__ dz, const T* __restrict__ logits, int64_t ldl,
+                              const float* __restrict__ lse, const int32_t* __restrict__ targets,
+                              int M, int V, float seed) {
   int64_t cpr = ldl / 8;
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)M * cpr) return;
   int row = (int)(idx / cpr);
   int c0 = (int)(idx % cpr) * 8;
-  T* z = logits + (int64_t)row * ldl + c0;
+  const T* z = logits + (int64_t)row * ldl + c0;
   float l = lse[row];
-  int y = targets[row];
+  int y = min(max(targets[row], 0), V - 1);  // clamped as in the forward
   float v[8];
   load8(z, v);
 #pragma unroll
@@ -733,15 +735,144 @@ __global__ void ce_bwd_kernel(T* __restrict__ logits, int64_t ldl, const float* 
     if (c == y) p -= 1.f;
     v[i] = p * seed;
   }
-  store8(z, v);
+  store8(dz + (int64_t)row * ldl + c0, v);
 }
 
-hipError_t crossentropy_backward(int dt, void* logits, int64_t ldl, const float* lse,
-                                 const int32_t* targets, int M, int V, float seed, hipStream_t s) {
-  if (ldl % 8 != 0) return hipErrorInvalidValue;
-  int64_t n = (int64_t)M * (ldl / 8);
-  DISPATCH_DT(dt, ce_bwd_kernel<T><<<grid_for(n, 256), 256, 0, s>>>((T*)logits, ldl, lse, targets,
-                                                                    M, V, seed));
+// The whole cross-entropy of a row in one workgroup of NT threads with the
+// row held in registers (NCHK 8-column chunks per thread, 8 NT columns
+// apart): first maximum and its column, sum of exp(z - max), then lse,
+// loss = lse - z_y, and dz = seed * (exp(z - lse) - [c == y]) (0 on the
+// padded columns), so the logits are read from memory once for the loss and
+// the gradient together.
+template <class T, int NT, int NCHK>
+__global__ __launch_bounds__(NT) void ce_fused_kernel(
+    float* __restrict__ losses, float* __restrict__ lse_out, int32_t* __restrict__ argmax_out,
+    T* __restrict__ dz, const T* __restrict__ logits, int64_t ldl,
+    const int32_t* __restrict__ targets, int V, float seed, int* __restrict__ flag) {
+  constexpr int NWV = NT / 64, STEP = NT * 8;
+  __shared__ SoftmaxState part[NWV];
+  __shared__ float lse_s;
+  __shared__ int y_s;
+  const int row = blockIdx.x;
+  const T* z = logits + (int64_t)row * ldl;
+  Raw8<T> r[NCHK];
+#pragma unroll
+  for (int c = 0; c < NCHK; ++c) {
+    const int c0 = threadIdx.x * 8 + c * STEP;
+    if (c0 < ldl) load_raw(z + c0, r[c]);  // c0 + 7 < ldl: ldl is a multiple of 8
+  }
+  float m = -INFINITY;
+  int arg = 0x7fffffff;
+#pragma unroll
+  for (int c = 0; c < NCHK; ++c) {
+    const int c0 = threadIdx.x * 8 + c * STEP;
+    if (c0 < V) {
+      float v[8];
+      unpack8(r[c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (c0 + i < V && v[i] > m) {  // first maximum in column order
+          m = v[i];
+          arg = c0 + i;
+        }
+    }
+  }
+  float sum = 0.f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < NCHK; ++c) {
+      const int c0 = threadIdx.x * 8 + c * STEP;
+      if (c0 < V) {
+        float v[8];
+        unpack8(r[c], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (c0 + i < V) sum += fast_exp(v[i] - m);
+      }
+    }
+  }
+  SoftmaxState st = {m, sum, arg};
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    SoftmaxState t;
+    t.m = __shfl_xor(st.m, o, 64);
+    t.s = __shfl_xor(st.s, o, 64);
+    t.arg = __shfl_xor(st.arg, o, 64);
+    st = sm_combine(st, t);
+  }
+  if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    SoftmaxState t = part[0];
+    for (int w = 1; w < NWV; ++w) t = sm_combine(t, part[w]);
+    const float lse = t.m + logf(t.s);
+    int y = targets[row];
+    if (y < 0 || y >= V) {
+      atomicOr(flag, 2);
+      y = y < 0 ? 0 : V - 1;
+    }
+    losses[row] = lse - to_f(z[y]);
+    lse_out[row] = lse;
+    argmax_out[row] = t.arg;
+    lse_s = lse;
+    y_s = y;
+  }
+  __syncthreads();
+  const float lse = lse_s;
+  const int y = y_s;
+  T* d = dz + (int64_t)row * ldl;
+#pragma unroll
+  for (int c = 0; c < NCHK; ++c) {
+    const int c0 = threadIdx.x * 8 + c * STEP;
+    if (c0 < ldl) {
+      float v[8], o[8];
+      unpack8(r[c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int cc = c0 + i;
+        float p = cc < V ? fast_exp(v[i] - lse) : 0.f;
+        if (cc == y) p -= 1.f;
+        o[i] = p * seed;
+      }
+      store8(d + c0, o);
+    }
+  }
+}
+
+// threads per row for wide rows (GPT-2's 50304 columns: 13 chunks each,
+// ~125 registers, two workgroups per CU)
+constexpr int CE_NT = 512;
+
+hipError_t crossentropy_fused(int dt, float* losses, float* lse, int32_t* argmax, void* dz,
+                              const void* logits, int64_t ldl, const int32_t* targets, int M,
+                              int V, float seed, int* err_flag, hipStream_t s) {
+  if (ldl % 8 != 0 || ldl < V) return hipErrorInvalidValue;
+#define CEF(T, NT, NC)                                                                         \
+  ce_fused_kernel<T, NT, NC><<<M, NT, 0, s>>>(losses, lse, argmax, (T*)dz, (const T*)logits,   \
+                                              ldl, targets, V, seed, err_flag)
+  // chunks per thread for 256 and for CE_NT threads per row
+  const int64_t nc256 = cdiv(ldl, 2048), nc = cdiv(ldl, 8 * CE_NT);
+  if (nc256 <= 1) {
+    if (dt == BF16) CEF(bf16, 256, 1);
+    else CEF(float, 256, 1);
+  } else if (nc256 <= 4) {
+    if (dt == BF16) CEF(bf16, 256, 4);
+    else CEF(float, 256, 4);
+  } else if (dt == BF16 && nc <= 7) {
+    CEF(bf16, CE_NT, 7);
+  } else if (dt == BF16 && nc <= 13) {
+    CEF(bf16, CE_NT, 13);  // GPT-2: 50304 columns
+  } else if (dt == BF16 && nc <= 16) {
+    CEF(bf16, CE_NT, 16);
+  } else {  // wider rows: the loss pass, then the gradient from a second read
+#undef CEF
+    hipError_t e = crossentropy_forward(dt, losses, lse, argmax, logits, ldl, targets, M, V,
+                                        err_flag, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)M * (ldl / 8);
+    DISPATCH_DT(dt, ce_bwd_kernel<T><<<grid_for(n, 256), 256, 0, s>>>(
+                        (T*)dz, (const T*)logits, ldl, lse, targets, M, V, seed));
+  }
   return hipGetLastError();
 }
 

@@ -686,6 +686,37 @@ __global__ void splitk_reduce_kernel(float* __restrict__ dst, int64_t ldo,
   *d = o;
 }
 
+// The same for up to four products in one launch (the grouped weight
+// gradients): product i owns the float4 indices q0[i] .. q0[i+1]-1.
+struct ReduceBatch {
+  int n, S;
+  float* dst[4];
+  int64_t ldo[4];
+  const float* part[4];
+  int M[4], N[4];
+  int64_t q0[5];
+};
+
+__global__ void splitk_reduce_group_kernel(const ReduceBatch rb) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= rb.q0[rb.n]) return;
+  int i = 0;
+  while (i + 1 < rb.n && q >= rb.q0[i + 1]) ++i;
+  const int M = rb.M[i], N = rb.N[i];
+  const int64_t total = (int64_t)M * N, idx = (q - rb.q0[i]) * 4;
+  const float* part = rb.part[i];
+  const int m = (int)(idx / N), n = (int)(idx % N);
+  float4 acc = *reinterpret_cast<const float4*>(part + idx);
+  for (int s = 1; s < rb.S; ++s) {
+    float4 p = *reinterpret_cast<const float4*>(part + (int64_t)s * total + idx);
+    acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+  }
+  float4* d = reinterpret_cast<float4*>(rb.dst[i] + (int64_t)m * rb.ldo[i] + n);
+  float4 o = *d;
+  o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+  *d = o;
+}
+
 // ================================================================ dispatch
 namespace {
 
@@ -914,15 +945,19 @@ hipError_t gemm_acc_group(int dt, int n, const AccItem* it, int K, void* ws, siz
     gemm_big_kernel<256, 256, false, false, EPI_ACC_F32><<<grid, 512, 0, s>>>(batch, K, kps);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || S == 1) return err;
+  ReduceBatch rb{};
+  rb.n = n;
+  rb.S = S;
   for (int i = 0; i < n; ++i) {
-    const BigProblem& p = batch.p[i];
-    const int64_t n4 = (int64_t)p.M * p.N / 4;
-    splitk_reduce_kernel<<<(unsigned)cdiv(n4, 256), 256, 0, s>>>(
-        it[i].out, it[i].ldo, (const float*)p.e.out, S, p.M, p.N);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    rb.dst[i] = it[i].out;
+    rb.ldo[i] = it[i].ldo;
+    rb.part[i] = (const float*)batch.p[i].e.out;
+    rb.M[i] = it[i].M;
+    rb.N[i] = it[i].N;
+    rb.q0[i + 1] = rb.q0[i] + (int64_t)it[i].M * it[i].N / 4;  // N % 4 == 0 here
   }
-  return hipSuccess;
+  splitk_reduce_group_kernel<<<(unsigned)cdiv(rb.q0[n], 256), 256, 0, s>>>(rb);
+  return hipGetLastError();
 }
 
 size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode) {

@@ -46,9 +46,12 @@ hipError_t crossentropy_forward(int dt, float* losses, float* lse, int32_t* argm
                                 const void* logits, int64_t ldl, const int32_t* targets, int M,
                                 int V, int* err_flag, hipStream_t s);
 hipError_t mean_loss(float* out, const float* losses, int M, hipStream_t s);
-// in place: logits <- seed * (softmax - onehot) for columns < V, 0 for V..ldl-1
-hipError_t crossentropy_backward(int dt, void* logits, int64_t ldl, const float* lse,
-                                 const int32_t* targets, int M, int V, float seed, hipStream_t s);
+// The forward above plus the logit gradient into dz (same pitch):
+// dz = seed * (softmax - onehot) for columns < V, 0 for V..ldl-1.  One read
+// of the logits when a row fits the workgroup's registers (bf16: ldl <= 65536).
+hipError_t crossentropy_fused(int dt, float* losses, float* lse, int32_t* argmax, void* dz,
+                              const void* logits, int64_t ldl, const int32_t* targets, int M,
+                              int V, float seed, int* err_flag, hipStream_t s);
 
 // ---- attention (qkv rows of 3C: [q | k | v], head h at h*hd)
 hipError_t attention_forward(int dt, void* out, float* lse, const void* qkv, int B, int T, int H,

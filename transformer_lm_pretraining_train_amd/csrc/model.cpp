@@ -149,6 +149,7 @@ struct gpt2_model {
   void* lnf;
   float *lnf_mean, *lnf_rstd;
   void* logits;
+  void* dlogits;  // d loss / d logits of the last forward with targets (same pitch)
   float *losses, *ce_lse, *loss_internal;
   int32_t* argmax;
   // backward
@@ -225,6 +226,7 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.lnf_mean = (float*)cv.take(M * 4);
   md.lnf_rstd = (float*)cv.take(M * 4);
   md.logits = cv.take(M * ldl * es);
+  md.dlogits = cv.take(M * ldl * es);
   md.losses = (float*)cv.take(M * 4);
   md.ce_lse = (float*)cv.take(M * 4);
   md.argmax = (int32_t*)cv.take(M * 4);
@@ -508,9 +510,11 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   TIMED(GPT2_TIMER_LM_HEAD_FWD, gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
                                      epi(EPI_STORE, md->logits, md->ldl), s));
   if (targets) {
-    TIMED(GPT2_TIMER_CE_FWD, crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax,
-                                                  md->logits, md->ldl, targets, M, md->V,
-                                                  md->err_flag, s));
+    // loss and, from the same read of the logits, their gradient for the backward
+    const float seed = (float)(1.0 / ((double)md->M * md->k));
+    TIMED(GPT2_TIMER_CE_FWD, crossentropy_fused(dt, md->losses, md->ce_lse, md->argmax,
+                                                md->dlogits, md->logits, md->ldl, targets, M,
+                                                md->V, seed, md->err_flag, s));
     LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
     md->have_targets = true;
   }
@@ -521,21 +525,18 @@ int gpt2_backward(gpt2_model* md) {
   if (!md) return fail(GPT2_EINVAL, "NULL model");
   if (!md->have_targets)
     return fail(GPT2_ESTATE, "backward needs a preceding forward with targets");
-  md->have_targets = false;  // logits are overwritten below
+  md->have_targets = false;
   const int dt = md->dt;
   const int C = md->C, H = md->H, M = (int)md->M;
   const Layout& Ly = md->lay;
   hipStream_t s = md->stream;
   float* P = md->params;
   float* G = md->grads;
-  const float seed = (float)(1.0 / ((double)md->M * md->k));
 
-  // d logits, in place (columns >= V become 0)
-  LAUNCH(crossentropy_backward(dt, md->logits, md->ldl, md->ce_lse, md->targets, M, md->V, seed, s));
-  // tied head: dwte += dz^T lnf ; dlnf = dz wte
-  LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->logits, md->ldl, md->lnf, C,
+  // tied head (d logits from the forward's cross-entropy): dwte += dz^T lnf ; dlnf = dz wte
+  LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->dlogits, md->ldl, md->lnf, C,
               epi(EPI_ACC_F32, G + Ly.wte, C), s, md->gemm_ws, md->gemm_ws_bytes));
-  LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->logits, md->ldl, md->wt(Ly.wte), C,
+  LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->dlogits, md->ldl, md->wt(Ly.wte), C,
               epi(EPI_STORE, md->dbuf_c, C), s));
   const void* xfinal = md->L > 0 ? md->act[md->L - 1].res3 : md->encoded;
   // The column sums of each residual gradient a LayerNorm backward produces
