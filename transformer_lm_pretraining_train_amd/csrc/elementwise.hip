@@ -481,19 +481,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // out_k[c] += sum_b partial[b * stride + k * C + c] for each non-null out_k
-// (k = 0, 1, 2), summed in a fixed order.  A workgroup covers 64 columns of
-// the concatenated outputs with 16 float4 lanes x 16 groups of partial rows
-// (group g sums rows g, g+16, ...); the 16 group sums are added in order.
+// (k = 0, 1, 2), summed in a fixed order.  A workgroup covers 16 columns of
+// the concatenated outputs with 4 float4 lanes x 64 groups of partial rows
+// (group g sums rows g, g+64, ...); the 64 group sums are added in order.
+// (16 columns per workgroup: 144-192 workgroups for the GPT-2 widths.)
 __global__ __launch_bounds__(256) void column_partials_reduce_kernel(
     float* __restrict__ out0, float* __restrict__ out1, float* __restrict__ out2,
     const float* __restrict__ partial, int nb, int C, int stride, int ncols) {
-  __shared__ float4 red[16][17];
-  const int q = threadIdx.x % 16, g = threadIdx.x / 16;
-  const int c = blockIdx.x * 64 + 4 * q;  // first of 4 columns (C % 4 == 0)
+  __shared__ float4 red[64][5];
+  const int q = threadIdx.x % 4, g = threadIdx.x / 4;
+  const int c = blockIdx.x * 16 + 4 * q;  // first of 4 columns (C % 4 == 0)
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < ncols) {
 #pragma unroll 4
-    for (int b = g; b < nb; b += 16) {
+    for (int b = g; b < nb; b += 64) {
       const float4 v = *reinterpret_cast<const float4*>(partial + (int64_t)b * stride + c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
@@ -502,8 +503,7 @@ __global__ __launch_bounds__(256) void column_partials_reduce_kernel(
   __syncthreads();
   if (g == 0 && c < ncols) {
     float4 t = red[0][q];
-#pragma unroll
-    for (int k = 1; k < 16; ++k) {
+    for (int k = 1; k < 64; ++k) {
       const float4 v = red[k][q];
       t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
     }
@@ -553,7 +553,7 @@ hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw
 #undef LNB
 #undef LNBH
   const int ncols = dsum ? 3 * C : 2 * C;
-  column_partials_reduce_kernel<<<grid_for(ncols, 64), 256, 0, s>>>(dw, db, dsum, partial, nb, C,
+  column_partials_reduce_kernel<<<grid_for(ncols, 16), 256, 0, s>>>(dw, db, dsum, partial, nb, C,
                                                                      3 * C, ncols);
   return hipGetLastError();
 }
@@ -603,7 +603,7 @@ hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ld
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)cdiv(M, BG_ROWS));
   float* partial = (float*)scratch;
   DISPATCH_DT(dt, bias_grad_kernel<T><<<grid, 256, 0, s>>>(partial, (const T*)dy, M, N, ldy));
-  column_partials_reduce_kernel<<<grid_for(N, 64), 256, 0, s>>>(db, nullptr, nullptr, partial,
+  column_partials_reduce_kernel<<<grid_for(N, 16), 256, 0, s>>>(db, nullptr, nullptr, partial,
                                                                  (int)grid.y, N, N, N);
   return hipGetLastError();
 }
@@ -700,7 +700,13 @@ __global__ __launch_bounds__(256) void mean_loss_kernel(float* __restrict__ out,
                                                         const float* __restrict__ losses, int M) {
   __shared__ double part[4];
   double acc = 0.0;
-  for (int i = threadIdx.x; i < M; i += 256) acc += losses[i];
+  const int M4 = M / 4;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < M4; i += 256) {  // 16-byte loads, several in flight
+    const float4 v = reinterpret_cast<const float4*>(losses)[i];
+    acc += (double)v.x + (double)v.y + (double)v.z + (double)v.w;
+  }
+  for (int i = 4 * M4 + threadIdx.x; i < M; i += 256) acc += losses[i];
   acc = wave_sum_d(acc);
   if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = acc;
   __syncthreads();
