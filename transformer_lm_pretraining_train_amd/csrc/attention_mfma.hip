@@ -212,36 +212,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 16; ++r)
           if (k0 + t * 32 + acc_row(r, h2) > myq) s[t][r] = -INFINITY;
     }
-    // row maximum as a tree (short dependency chains)
-    float m8[8];
+    // Probabilities against the current reference m first; the tile's
+    // maximum is needed only when some probability is too large (a score
+    // more than 2^RESCALE_LOG2 above the reference: the partial sums show
+    // it, and an infinite m - score or a first tile gives inf or NaN there).
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
+    float pe[2][16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      m8[i] = fmaxf(fmaxf(s[i / 4][4 * (i % 4)], s[i / 4][4 * (i % 4) + 1]),
-                    fmaxf(s[i / 4][4 * (i % 4) + 2], s[i / 4][4 * (i % 4) + 3]));
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
-    float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-    // move the reference only when this tile exceeds it by more than 2^8
-    const bool move = mx > m + RESCALE_LOG2;
-    if (__builtin_amdgcn_ballot_w64(move)) {
+      for (int r = 0; r < 16; ++r) {
+        pe[t][r] = exp2_(__builtin_fmaf(s[t][r], c, -m));
+        ps[r % 4] += pe[t][r];
+      }
+    float tsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // !(x <= bound) is also true for NaN
+    if (__builtin_amdgcn_ballot_w64(!(tsum <= 64.0f * (1 << (int)RESCALE_LOG2)))) {
+      // row maximum as a tree (short dependency chains)
+      float m8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        m8[i] = fmaxf(fmaxf(s[i / 4][4 * (i % 4)], s[i / 4][4 * (i % 4) + 1]),
+                      fmaxf(s[i / 4][4 * (i % 4) + 2], s[i / 4][4 * (i % 4) + 3]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m8[i] = fmaxf(m8[i], m8[i + 4]);
+      float mx = fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      // move the reference only when this tile exceeds it by more than 2^8
+      const bool move = mx > m + RESCALE_LOG2;
       const float mnew = move ? mx : m;
       const float alpha = exp2_(m - mnew);
       m = mnew;
       l *= alpha;
       o[0] *= alpha;
       o[1] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[i] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pe[t][r] = exp2_(__builtin_fmaf(s[t][r], c, -m));
+          ps[r % 4] += pe[t][r];
+        }
+      tsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     }
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_(__builtin_fmaf(s[t][r], c, -m));
-        s[t][r] = p;
-        ps[r % 4] += p;
-      }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      for (int r = 0; r < 16; ++r) s[t][r] = pe[t][r];
+    l += tsum;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
