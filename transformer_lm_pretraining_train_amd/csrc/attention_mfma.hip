@@ -157,10 +157,14 @@ __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x
 // --------------------------------------------------------------- forward
 // Online softmax with a lazily moved reference: each query keeps a running
 // reference m (log2 units) and accumulates l = sum exp2(s c - m) and
-// O = sum exp2(s c - m) v.  m is raised only when a tile's maximum exceeds it
-// by more than 8, so the probabilities stay below 2^8 (no fp32 overflow) and
-// most tiles skip the rescaling of O; l and O always share the same m, so the
-// result O / l and the log-sum-exp m + log2 l are exact.
+// O = sum exp2(s c - m) v.  A tile's probabilities are first taken against
+// the current m; only when a query's sum over the tile exceeds 64 * 2^8 (or
+// is not finite: the first tile, m = -inf) is the tile's maximum computed,
+// m raised to it if it exceeds m by more than 8, O and l rescaled and the
+// probabilities recomputed.  So every probability stays below 2^14 (no fp32
+// overflow), most tiles need neither the maximum nor a rescale, and since l
+// and O always share the same m, O / l and the log-sum-exp m + log2 l are
+// exact.
 constexpr float RESCALE_LOG2 = 8.0f;
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_mfma(
