@@ -50,9 +50,9 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
                void* dev_out2, int64_t ldo2, const void* dev_aux, int64_t ldx, void* dev_ws,
                size_t ws_bytes, void* hip_stream);
 
-/* Weight gradients of up to four linear layers over the same K tokens:
+/* Weight gradients of up to eight linear layers over the same K tokens:
  * out_i(m, n) += sum_{k < K} A_i[k*lda_i + m] B_i[k*ldb_i + n] for
- * m < M_i, n < N_i, i < n, 1 <= n <= 4 (dW += dy^T x with dy, x stored
+ * m < M_i, n < N_i, i < n, 1 <= n <= 8 (dW += dy^T x with dy, x stored
  * row-major; "Let's reproduce GPT-2 (124M)": the backward pass of each
  * linear layer).  M, N, lda, ldb, ldo are host arrays of n entries; dev_A,
  * dev_B, dev_out host arrays of n device pointers; out_i is fp32, A_i and
@@ -61,7 +61,7 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
  * scratch is given in dev_ws; otherwise (and in fp32) as gpt2k_gemm calls
  * with GPT2K_EPI_ACC_F32, one per product.  The products' outputs must not
  * overlap each other or their inputs.  Returns GPT2_EINVAL for n outside
- * 1..4, a NULL pointer, negative sizes or pitches not multiples of 8. */
+ * 1..8, a NULL pointer, negative sizes or pitches not multiples of 8. */
 size_t gpt2k_gemm_acc_group_workspace_bytes(int dtype, int n, const int* M, const int* N, int K,
                                             const int64_t* lda, const int64_t* ldb);
 int gpt2k_gemm_acc_group(int dtype, int n, const int* M, const int* N, int K,

@@ -478,8 +478,8 @@ struct BigSmem {
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // One product of a launch.  Up to kMaxGroup products with the same K and
-// operand orientations share a launch, gridDim.z selecting the product
-// (the weight gradients of one layer run as one launch this way).
+// operand orientations share a launch (the weight gradients of one or two
+// layers run as one launch this way).
 struct BigProblem {
   int M, N, tiles_m, tiles_n;
   const bf16* A;
@@ -488,7 +488,7 @@ struct BigProblem {
   int64_t ldb;
   Epilogue e;
 };
-constexpr int kMaxGroup = 4;
+constexpr int kMaxGroup = 8;
 struct BigBatch {
   BigProblem p[kMaxGroup];
   // Grouped launches (grouped != 0): a 1-D grid of work items, product i owning
@@ -686,15 +686,15 @@ __global__ void splitk_reduce_kernel(float* __restrict__ dst, int64_t ldo,
   *d = o;
 }
 
-// The same for up to four products in one launch (the grouped weight
+// The same for up to kMaxGroup products in one launch (the grouped weight
 // gradients): product i owns the float4 indices q0[i] .. q0[i+1]-1.
 struct ReduceBatch {
   int n, S;
-  float* dst[4];
-  int64_t ldo[4];
-  const float* part[4];
-  int M[4], N[4];
-  int64_t q0[5];
+  float* dst[kMaxGroup];
+  int64_t ldo[kMaxGroup];
+  const float* part[kMaxGroup];
+  int M[kMaxGroup], N[kMaxGroup];
+  int64_t q0[kMaxGroup + 1];
 };
 
 __global__ void splitk_reduce_group_kernel(const ReduceBatch rb) {
@@ -866,8 +866,10 @@ int acc_row_split(int dt, int M, int N, int K, int mode) {
 // than the CUs; run as one launch, their tiles together fill the chip with
 // a split of K into S parts (S from the total tile count), so that the
 // partial tiles cost S x (sum of M_i N_i) floats instead of each product's
-// own, larger split.  Returns 0 where the grouped launch does not apply.
-static int acc_group_splits(int dt, int n, const AccItem* it, int K) {
+// own, larger split; two layers' (216 tiles at GPT-2 124M) need no split at
+// all.  Returns the split, or 0 where the grouped launch does not apply
+// (more tiles than CUs, fp32, pitches or spans it cannot address).
+int gemm_acc_group_splits(int dt, int n, const AccItem* it, int K) {
   if (dt != BF16 || n < 1 || n > kMaxGroup || K % 8 != 0 || K <= 0) return 0;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) {
@@ -885,7 +887,7 @@ static int acc_group_splits(int dt, int n, const AccItem* it, int K) {
 }
 
 size_t gemm_acc_group_workspace_bytes(int dt, int n, const AccItem* it, int K) {
-  const int S = acc_group_splits(dt, n, it, K);
+  const int S = gemm_acc_group_splits(dt, n, it, K);
   if (S <= 1) return 0;
   size_t t = 0;
   for (int i = 0; i < n; ++i) t += round_up((int64_t)it[i].M * it[i].N, 64) * sizeof(float);
@@ -894,7 +896,7 @@ size_t gemm_acc_group_workspace_bytes(int dt, int n, const AccItem* it, int K) {
 
 hipError_t gemm_acc_group(int dt, int n, const AccItem* it, int K, void* ws, size_t ws_bytes,
                           hipStream_t s) {
-  int S = acc_group_splits(dt, n, it, K);
+  int S = gemm_acc_group_splits(dt, n, it, K);
   bool vec4 = true;
   for (int i = 0; i < n; ++i) vec4 = vec4 && it[i].N % 4 == 0 && it[i].ldo % 4 == 0;
   if (S > 1 && (!ws || ws_bytes < gemm_acc_group_workspace_bytes(dt, n, it, K) || !vec4)) S = 0;

@@ -105,8 +105,10 @@ struct AccItem {
   float* out;
   int64_t ldo;
 };
-// Up to four such products with a common K in one launch (bf16), else one
+// Up to eight such products with a common K in one launch (bf16), else one
 // gemm() each; split-K partials need gemm_acc_group_workspace_bytes() in ws.
+// gemm_acc_group_splits: the K split of that launch, 0 if it does not apply.
+int gemm_acc_group_splits(int dt, int n, const AccItem* items, int K);
 size_t gemm_acc_group_workspace_bytes(int dt, int n, const AccItem* items, int K);
 hipError_t gemm_acc_group(int dt, int n, const AccItem* items, int K, void* ws, size_t ws_bytes,
                           hipStream_t s);

@@ -59,7 +59,7 @@ size_t gpt2k_gemm_workspace_bytes(int dtype, int M, int N, int K, int epilogue) 
 
 static bool acc_items(int n, const int* M, const int* N, const int64_t* lda, const int64_t* ldb,
                       AccItem* it) {
-  if (n < 1 || n > 4 || !M || !N || !lda || !ldb) return false;
+  if (n < 1 || n > 8 || !M || !N || !lda || !ldb) return false;
   for (int i = 0; i < n; ++i) {
     if (M[i] < 0 || N[i] < 0 || lda[i] % 8 || ldb[i] % 8) return false;
     it[i] = AccItem{M[i], N[i], nullptr, lda[i], nullptr, ldb[i], nullptr, 0};
@@ -69,7 +69,7 @@ static bool acc_items(int n, const int* M, const int* N, const int64_t* lda, con
 
 size_t gpt2k_gemm_acc_group_workspace_bytes(int dtype, int n, const int* M, const int* N, int K,
                                             const int64_t* lda, const int64_t* ldb) {
-  AccItem it[4];
+  AccItem it[8];
   if (!acc_items(n, M, N, lda, ldb, it) || K < 0) return 0;
   return gemm_acc_group_workspace_bytes(dtype, n, it, K);
 }
@@ -80,7 +80,7 @@ int gpt2k_gemm_acc_group(int dtype, int n, const int* M, const int* N, int K, co
                          void* stream) {
   if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
     return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
-  AccItem it[4];
+  AccItem it[8];
   if (!acc_items(n, M, N, lda, ldb, it) || K < 0 || !A || !B || !out || !ldo)
     return gpt2_internal_fail(GPT2_EINVAL, "bad group: n, sizes, pitches or NULL arrays");
   for (int i = 0; i < n; ++i) {

@@ -153,7 +153,13 @@ struct gpt2_model {
   float *losses, *ce_lse, *loss_internal;
   int32_t* argmax;
   // backward
-  void *dres, *dres2, *dbuf_c, *dbuf_4c, *dqkv;  // dres, dres2: residual gradient, ping-pong
+  // Backward buffers.  Per layer: d res3 (the layer's input gradient from
+  // above), d res2, d fch and d qkv, in two sets used by alternate layers so
+  // that one layer's are still intact while the next is computed (the
+  // weight gradients of two layers run together); dres: d x of the first
+  // layer (the embedding gradient); dbuf_c: scratch activation gradient.
+  void *bw_in[2], *bw_mid[2], *bw_d4[2], *bw_dq[2];
+  void *dres, *dbuf_c;
   void* scratch;
   void* gemm_ws;  // split-K partial tiles of the weight-gradient GEMMs
   size_t gemm_ws_bytes;
@@ -231,11 +237,14 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.ce_lse = (float*)cv.take(M * 4);
   md.argmax = (int32_t*)cv.take(M * 4);
   md.loss_internal = (float*)cv.take(4);
+  for (int i = 0; i < 2; ++i) {
+    md.bw_in[i] = cv.take(M * C * es);
+    md.bw_mid[i] = cv.take(M * C * es);
+    md.bw_d4[i] = cv.take(M * 4 * C * es);
+    md.bw_dq[i] = cv.take(M * 3 * C * es);
+  }
   md.dres = cv.take(M * C * es);
-  md.dres2 = cv.take(M * C * es);
   md.dbuf_c = cv.take(M * C * es);
-  md.dbuf_4c = cv.take(M * 4 * C * es);
-  md.dqkv = cv.take(M * 3 * C * es);
   size_t sc = layernorm_backward_scratch_bytes((int)M, (int)C);
   sc = std::max(sc, bias_grad_scratch_bytes((int)M, (int)(4 * C)));
   sc = std::max(sc, attention_backward_scratch_bytes(c.micro_batch, c.seq_len, H));
@@ -543,57 +552,81 @@ int gpt2_backward(gpt2_model* md) {
   // are the bias gradient of the linear layer that wrote that residual:
   // fc-proj of the layer below (res3) or proj of the same layer (res2).
   float* fcp_b_below = md->L > 0 ? G + Ly.layers[md->L - 1].fcp_b : nullptr;
-  // The residual gradient alternates between two buffers: each layer reads
-  // d res3 from `cur` and leaves d x in `nxt`, so that d res3 is still there
-  // when the layer's weight gradients run together at its end.
-  void* cur = md->dres;
-  void* nxt = md->dres2;
-  LAUNCH(layernorm_backward(dt, cur, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
+  // Layer l works in buffer set l % 2: in (d res3, from the layer above),
+  // mid (d res2), d4 (d fch), dq (d qkv).  Its four weight gradients are
+  // queued and launched together with the next layer's (one launch of
+  // eight products when their tiles fit the chip in one round, else four at
+  // a time), before that layer's LayerNorm-1 backward overwrites set l % 2.
+  const int Lh = md->L;
+  void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 2] : md->dres;
+  LAUNCH(layernorm_backward(dt, top, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
                             md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
                             md->scratch, s));
-  for (int l = md->L - 1; l >= 0; --l) {
+  AccItem pend[8];
+  int npend = 0;
+  for (int l = Lh - 1; l >= 0; --l) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
     const void* xin = l > 0 ? md->act[l - 1].res3 : md->encoded;
-    // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b; cur = d res3
-    Epilogue e = epi(EPI_GELU_BWD, md->dbuf_4c, 4 * C);
+    void* in = md->bw_in[l % 2];
+    void* mid = md->bw_mid[l % 2];
+    void* d4 = md->bw_d4[l % 2];
+    void* dq = md->bw_dq[l % 2];
+    // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
+    Epilogue e = epi(EPI_GELU_BWD, d4, 4 * C);
     e.aux = a.fch;
     e.ldx = 4 * C;
-    LAUNCH(gemm(dt, true, false, M, 4 * C, C, cur, C, md->wt(o.fcp_w), 4 * C, e, s));
-    // fc: fch = ln2 fc_w^T + fc_b  (dbuf_4c now holds d fch; its column sums
-    // are taken right after the product that reads it)
-    LAUNCH(gemm(dt, true, false, M, C, 4 * C, md->dbuf_4c, 4 * C, md->wt(o.fc_w), C,
+    LAUNCH(gemm(dt, true, false, M, 4 * C, C, in, C, md->wt(o.fcp_w), 4 * C, e, s));
+    // fc: fch = ln2 fc_w^T + fc_b  (d4 holds d fch; its column sums are taken
+    // right after the product that reads it)
+    LAUNCH(gemm(dt, true, false, M, C, 4 * C, d4, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(bias_grad(dt, G + o.fc_b, md->dbuf_4c, M, 4 * C, 4 * C, md->scratch, s));
-    // nxt = d res2 = d res3 + the LayerNorm-2 backward
-    LAUNCH(layernorm_backward(dt, nxt, cur, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
+    LAUNCH(bias_grad(dt, G + o.fc_b, d4, M, 4 * C, 4 * C, md->scratch, s));
+    // mid = d res2 = d res3 + the LayerNorm-2 backward
+    LAUNCH(layernorm_backward(dt, mid, in, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
                               md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
                               md->scratch, s));
     // attention output projection: res2 = x + atty proj_w^T + proj_b
-    LAUNCH(gemm(dt, true, false, M, C, C, nxt, C, md->wt(o.proj_w), C,
+    LAUNCH(gemm(dt, true, false, M, C, C, mid, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    TIMED(GPT2_TIMER_ATTN_BWD, attention_backward(dt, md->dqkv, md->dbuf_c, a.qkv, a.atty, a.lse,
+    TIMED(GPT2_TIMER_ATTN_BWD, attention_backward(dt, dq, md->dbuf_c, a.qkv, a.atty, a.lse,
                                                   md->B, md->Tn, H, md->hd, md->scratch, s));
     // qkv = ln1 qkv_w^T + qkv_b
-    LAUNCH(gemm(dt, true, false, M, C, 3 * C, md->dqkv, 3 * C, md->wt(o.qkv_w), C,
+    LAUNCH(gemm(dt, true, false, M, C, 3 * C, dq, 3 * C, md->wt(o.qkv_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(bias_grad(dt, G + o.qkv_b, md->dqkv, M, 3 * C, 3 * C, md->scratch, s));
-    // the layer's weight gradients dW += dy^T x, as one launch
+    LAUNCH(bias_grad(dt, G + o.qkv_b, dq, M, 3 * C, 3 * C, md->scratch, s));
+    // the layer's weight gradients dW += dy^T x
     const AccItem dw[4] = {
-        {C, 4 * C, cur, C, a.fchg, 4 * C, G + o.fcp_w, 4 * C},
-        {4 * C, C, md->dbuf_4c, 4 * C, a.ln2, C, G + o.fc_w, C},
-        {C, C, nxt, C, a.atty, C, G + o.proj_w, C},
-        {3 * C, C, md->dqkv, 3 * C, a.ln1, C, G + o.qkv_w, C}};
-    LAUNCH(gemm_acc_group(dt, 4, dw, M, md->gemm_ws, md->gemm_ws_bytes, s));
-    // nxt = d x = d res2 + the LayerNorm-1 backward
-    LAUNCH(layernorm_backward(dt, nxt, nxt, G + o.ln1_w, G + o.ln1_b,
+        {C, 4 * C, in, C, a.fchg, 4 * C, G + o.fcp_w, 4 * C},
+        {4 * C, C, d4, 4 * C, a.ln2, C, G + o.fc_w, C},
+        {C, C, mid, C, a.atty, C, G + o.proj_w, C},
+        {3 * C, C, dq, 3 * C, a.ln1, C, G + o.qkv_w, C}};
+    std::copy(dw, dw + 4, pend + npend);
+    npend += 4;
+    if (npend == 8) {
+      if (gemm_acc_group_splits(dt, 8, pend, M) > 0) {  // both layers in one round of tiles
+        LAUNCH(gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        npend = 0;
+      } else {  // the layer above alone; this one waits for the next
+        LAUNCH(gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        std::copy(pend + 4, pend + 8, pend);
+        npend = 4;
+      }
+    }
+    if (l == 0 && npend > 0) {
+      LAUNCH(gemm_acc_group(dt, npend, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+      npend = 0;
+    }
+    // d x = d res2 + the LayerNorm-1 backward, into the next layer's input
+    // buffer (the other set), or for the first layer the embedding gradient
+    void* dx = l > 0 ? md->bw_in[(l - 1) % 2] : md->dres;
+    LAUNCH(layernorm_backward(dt, dx, mid, G + o.ln1_w, G + o.ln1_b,
                               l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c, xin,
                               a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, md->scratch, s));
-    std::swap(cur, nxt);
   }
   // embeddings
-  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, cur, md->tokens, M, C, md->V, md->scratch, s));
-  LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, cur, md->B, md->Tn, C, s));
+  LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
+  LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, md->dres, md->B, md->Tn, C, s));
   return GPT2_OK;
 }
 
