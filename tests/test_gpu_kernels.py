@@ -248,6 +248,14 @@ def test_weight_gradient_group_ragged(K):
     _acc_group_case(BF16, [(384, 1536), (1536, 384), (384, 384), (1152, 384)], K, 12)
 
 
+def test_weight_gradients_of_two_layers_in_one_launch():
+    """Eight products (two 124M layers): 216 tiles in one round, no K split;
+    K = 1000 leaves a partial last k-tile."""
+    layer = [(768, 3072), (3072, 768), (768, 768), (2304, 768)]
+    nb = _acc_group_case(BF16, layer + layer, 1000, 17)
+    assert nb == 0  # no split, no partials
+
+
 def test_weight_gradient_group_fallbacks():
     """Without workspace, with one or three products, and in fp32 (one
     product per launch) the results are the same products."""
