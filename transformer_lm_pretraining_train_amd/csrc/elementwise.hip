@@ -7,6 +7,8 @@
 // (shuffles) or a workgroup (LDS); column reductions (LayerNorm gain/shift
 // and bias gradients) are two-stage with partials in a scratch buffer and a
 // fixed summation order, so they are bitwise repeatable.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -485,30 +487,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // the concatenated outputs with 4 float4 lanes x 64 groups of partial rows
 // (group g sums rows g, g+64, ...); the 64 group sums are added in order.
 // (16 columns per workgroup: 144-192 workgroups for the GPT-2 widths.)
-__global__ __launch_bounds__(256) void column_partials_reduce_kernel(
-    float* __restrict__ out0, float* __restrict__ out1, float* __restrict__ out2,
-    const float* __restrict__ partial, int nb, int C, int stride, int ncols) {
+__device__ __forceinline__ void column_reduce_block(const ColReduce& d, int blk) {
   __shared__ float4 red[64][5];
   const int q = threadIdx.x % 4, g = threadIdx.x / 4;
-  const int c = blockIdx.x * 16 + 4 * q;  // first of 4 columns (C % 4 == 0)
+  const int c = blk * 16 + 4 * q;  // first of 4 columns (C % 4 == 0)
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < ncols) {
+  if (c < d.ncols) {
 #pragma unroll 4
-    for (int b = g; b < nb; b += 64) {
-      const float4 v = *reinterpret_cast<const float4*>(partial + (int64_t)b * stride + c);
+    for (int b = g; b < d.nb; b += 64) {
+      const float4 v = *reinterpret_cast<const float4*>(d.partial + (int64_t)b * d.stride + c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
   }
   red[g][q] = acc;
   __syncthreads();
-  if (g == 0 && c < ncols) {
+  if (g == 0 && c < d.ncols) {
     float4 t = red[0][q];
     for (int k = 1; k < 64; ++k) {
       const float4 v = red[k][q];
       t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
     }
-    const int k = c / C, cc = c % C;
-    float* o = k == 0 ? out0 : k == 1 ? out1 : out2;
+    const int k = c / d.C, cc = c % d.C;
+    float* o = k == 0 ? d.out0 : k == 1 ? d.out1 : d.out2;
     if (o) {
       float4* op = reinterpret_cast<float4*>(o + cc);
       float4 cur = *op;
@@ -516,6 +516,44 @@ __global__ __launch_bounds__(256) void column_partials_reduce_kernel(
       *op = cur;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void column_partials_reduce_kernel(const ColReduce d) {
+  column_reduce_block(d, blockIdx.x);
+}
+
+// Several reductions in one launch: descriptor i owns workgroups blk0[i] ..
+// blk0[i+1]-1.
+constexpr int kColBatch = 32;
+struct ColBatch {
+  ColReduce d[kColBatch];
+  int n;
+  int blk0[kColBatch + 1];
+};
+__global__ __launch_bounds__(256) void column_reduce_batch_kernel(const ColBatch cb) {
+  int i = 0;
+  while (i + 1 < cb.n && (int)blockIdx.x >= cb.blk0[i + 1]) ++i;
+  column_reduce_block(cb.d[i], blockIdx.x - cb.blk0[i]);
+}
+
+static hipError_t column_reduce(const ColReduce& d, hipStream_t s) {
+  column_partials_reduce_kernel<<<grid_for(d.ncols, 16), 256, 0, s>>>(d);
+  return hipGetLastError();
+}
+
+hipError_t column_reduce_batched(const ColReduce* d, int n, hipStream_t s) {
+  for (int i0 = 0; i0 < n; i0 += kColBatch) {
+    ColBatch cb{};
+    cb.n = std::min(kColBatch, n - i0);
+    for (int i = 0; i < cb.n; ++i) {
+      cb.d[i] = d[i0 + i];
+      cb.blk0[i + 1] = cb.blk0[i] + grid_for(d[i0 + i].ncols, 16);
+    }
+    if (cb.blk0[cb.n] > 0) column_reduce_batch_kernel<<<cb.blk0[cb.n], 256, 0, s>>>(cb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 size_t layernorm_backward_scratch_bytes(int M, int C) {
@@ -526,7 +564,7 @@ hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw
                               float* dsum, bool accumulate, const void* dy, const void* inp,
                               const float* mean,
                               const float* rstd, const float* w, int M, int C, void* scratch,
-                              hipStream_t s) {
+                              hipStream_t s, ColReduce* defer) {
   if (C % 8 != 0 || C > 8 * 64 * LN_MAXCH) return hipErrorInvalidValue;
   const int nb = (int)cdiv(M, LNB_ROWS);
   float* partial = (float*)scratch;
@@ -552,10 +590,12 @@ hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw
   else LNB(4);
 #undef LNB
 #undef LNBH
-  const int ncols = dsum ? 3 * C : 2 * C;
-  column_partials_reduce_kernel<<<grid_for(ncols, 16), 256, 0, s>>>(dw, db, dsum, partial, nb, C,
-                                                                     3 * C, ncols);
-  return hipGetLastError();
+  const ColReduce d{dw, db, dsum, partial, nb, C, 3 * C, dsum ? 3 * C : 2 * C};
+  if (defer) {
+    *defer = d;
+    return hipGetLastError();
+  }
+  return column_reduce(d, s);
 }
 
 // =========================================================== bias gradient
@@ -598,14 +638,17 @@ size_t bias_grad_scratch_bytes(int M, int N) {
 }
 
 hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ldy, void* scratch,
-                     hipStream_t s) {
+                     hipStream_t s, ColReduce* defer) {
   if (N % 8 != 0 || ldy % 8 != 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)cdiv(N, 256), (unsigned)cdiv(M, BG_ROWS));
   float* partial = (float*)scratch;
   DISPATCH_DT(dt, bias_grad_kernel<T><<<grid, 256, 0, s>>>(partial, (const T*)dy, M, N, ldy));
-  column_partials_reduce_kernel<<<grid_for(N, 16), 256, 0, s>>>(db, nullptr, nullptr, partial,
-                                                                 (int)grid.y, N, N, N);
-  return hipGetLastError();
+  const ColReduce d{db, nullptr, nullptr, partial, (int)grid.y, N, N, N};
+  if (defer) {
+    *defer = d;
+    return hipGetLastError();
+  }
+  return column_reduce(d, s);
 }
 
 // =========================================================== cross-entropy

@@ -23,23 +23,39 @@ size_t encoder_backward_wte_scratch_bytes(int M, int V, int C);
 hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32_t* tok, int M,
                                 int C, int V, void* scratch, hipStream_t s);
 
+// ---- fixed-order column reductions of partial sums
+// out_k[c] += sum_{b < nb} partial[b * stride + k * C + c] for c < ncols
+// (k = c / C selects out0, out1 or out2; a null out_k is skipped).
+struct ColReduce {
+  float* out0;
+  float* out1;
+  float* out2;
+  const float* partial;
+  int nb, C, stride, ncols;
+};
+// Several such reductions in as few launches as possible (the LayerNorm and
+// bias-gradient column sums of a whole backward pass, deferred to its end).
+hipError_t column_reduce_batched(const ColReduce* d, int n, hipStream_t s);
+
 // ---- LayerNorm
 hipError_t layernorm_forward(int dt, void* out, float* mean, float* rstd, const void* inp,
                              const float* w, const float* b, int M, int C, float eps, hipStream_t s);
 // dres = dx (accumulate false) or dres = dres_in + dx (dres_in null or
 // equal to dres: in place); dw, db += column sums of dy*xhat and dy; dsum
 // (if not null) += column sums of the new dres.  Two-stage, partials in
-// scratch.
+// scratch.  With `defer` the partials stay in scratch and their reduction
+// is returned in *defer instead of being launched.
 size_t layernorm_backward_scratch_bytes(int M, int C);
 hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw, float* db,
                               float* dsum, bool accumulate, const void* dy, const void* inp,
                               const float* mean, const float* rstd, const float* w, int M, int C,
-                              void* scratch, hipStream_t s);
+                              void* scratch, hipStream_t s, ColReduce* defer = nullptr);
 
 // ---- bias gradient: db[n] += sum_m dy[m, n] (two-stage, partials in scratch)
 size_t bias_grad_scratch_bytes(int M, int N);
 hipError_t bias_grad(int dt, float* db, const void* dy, int M, int N, int64_t ldy, void* scratch,
-                     hipStream_t s);
+                     hipStream_t s,
+                     ColReduce* defer = nullptr);
 
 // ---- cross-entropy over the padded vocabulary (row pitch ldl >= Vp)
 hipError_t crossentropy_forward(int dt, float* losses, float* lse, int32_t* argmax,

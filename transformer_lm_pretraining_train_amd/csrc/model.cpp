@@ -161,6 +161,11 @@ struct gpt2_model {
   void *bw_in[2], *bw_mid[2], *bw_d4[2], *bw_dq[2];
   void *dres, *dbuf_c;
   void* scratch;
+  // Column partial sums of every LayerNorm backward and bias gradient of a
+  // backward pass, each in its own slot; one batched reduction at the end.
+  void* colpart;
+  size_t ln_slot, bg_slot;  // bytes per LayerNorm / bias-gradient slot
+  std::vector<ColReduce> cols;
   void* gemm_ws;  // split-K partial tiles of the weight-gradient GEMMs
   size_t gemm_ws_bytes;
   void* norm_scratch;
@@ -250,6 +255,10 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   sc = std::max(sc, attention_backward_scratch_bytes(c.micro_batch, c.seq_len, H));
   sc = std::max(sc, encoder_backward_wte_scratch_bytes((int)M, c.vocab_size, (int)C));
   md.scratch = cv.take(sc);
+  md.ln_slot = (layernorm_backward_scratch_bytes((int)M, (int)C) + kAlign - 1) / kAlign * kAlign;
+  md.bg_slot = (bias_grad_scratch_bytes((int)M, (int)(4 * C)) + kAlign - 1) / kAlign * kAlign;
+  md.colpart = cv.take((size_t)(2 * c.n_layer + 1) * md.ln_slot + (size_t)(2 * c.n_layer) * md.bg_slot);
+  md.cols.reserve(4 * c.n_layer + 1);
   size_t gw = 0;
   {
     const int Mi = (int)M, Ci = (int)C;
@@ -542,6 +551,22 @@ int gpt2_backward(gpt2_model* md) {
   float* P = md->params;
   float* G = md->grads;
 
+  // Column sums (LayerNorm gain/shift, biases) are written as partials into
+  // their own slots and reduced together after the layer loop.
+  md->cols.clear();
+  char* colslot = (char*)md->colpart;
+  auto ln_part = [&]() {
+    void* p = colslot;
+    colslot += md->ln_slot;
+    md->cols.emplace_back();
+    return p;
+  };
+  auto bg_part = [&]() {
+    void* p = colslot;
+    colslot += md->bg_slot;
+    md->cols.emplace_back();
+    return p;
+  };
   // tied head (d logits from the forward's cross-entropy): dwte += dz^T lnf ; dlnf = dz wte
   LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->dlogits, md->ldl, md->lnf, C,
               epi(EPI_ACC_F32, G + Ly.wte, C), s, md->gemm_ws, md->gemm_ws_bytes));
@@ -559,9 +584,12 @@ int gpt2_backward(gpt2_model* md) {
   // a time), before that layer's LayerNorm-1 backward overwrites set l % 2.
   const int Lh = md->L;
   void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 2] : md->dres;
-  LAUNCH(layernorm_backward(dt, top, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
-                            md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
-                            md->scratch, s));
+  {
+    void* slot = ln_part();
+    LAUNCH(layernorm_backward(dt, top, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
+                              md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
+                              slot, s, &md->cols.back()));
+  }
   AccItem pend[8];
   int npend = 0;
   for (int l = Lh - 1; l >= 0; --l) {
@@ -581,11 +609,17 @@ int gpt2_backward(gpt2_model* md) {
     // right after the product that reads it)
     LAUNCH(gemm(dt, true, false, M, C, 4 * C, d4, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(bias_grad(dt, G + o.fc_b, d4, M, 4 * C, 4 * C, md->scratch, s));
+    {
+      void* slot = bg_part();
+      LAUNCH(bias_grad(dt, G + o.fc_b, d4, M, 4 * C, 4 * C, slot, s, &md->cols.back()));
+    }
     // mid = d res2 = d res3 + the LayerNorm-2 backward
-    LAUNCH(layernorm_backward(dt, mid, in, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
-                              md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
-                              md->scratch, s));
+    {
+      void* slot = ln_part();
+      LAUNCH(layernorm_backward(dt, mid, in, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
+                                md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
+                                slot, s, &md->cols.back()));
+    }
     // attention output projection: res2 = x + atty proj_w^T + proj_b
     LAUNCH(gemm(dt, true, false, M, C, C, mid, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
@@ -594,7 +628,10 @@ int gpt2_backward(gpt2_model* md) {
     // qkv = ln1 qkv_w^T + qkv_b
     LAUNCH(gemm(dt, true, false, M, C, 3 * C, dq, 3 * C, md->wt(o.qkv_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    LAUNCH(bias_grad(dt, G + o.qkv_b, dq, M, 3 * C, 3 * C, md->scratch, s));
+    {
+      void* slot = bg_part();
+      LAUNCH(bias_grad(dt, G + o.qkv_b, dq, M, 3 * C, 3 * C, slot, s, &md->cols.back()));
+    }
     // the layer's weight gradients dW += dy^T x
     const AccItem dw[4] = {
         {C, 4 * C, in, C, a.fchg, 4 * C, G + o.fcp_w, 4 * C},
@@ -620,10 +657,15 @@ int gpt2_backward(gpt2_model* md) {
     // d x = d res2 + the LayerNorm-1 backward, into the next layer's input
     // buffer (the other set), or for the first layer the embedding gradient
     void* dx = l > 0 ? md->bw_in[(l - 1) % 2] : md->dres;
-    LAUNCH(layernorm_backward(dt, dx, mid, G + o.ln1_w, G + o.ln1_b,
-                              l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c, xin,
-                              a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, md->scratch, s));
+    {
+      void* slot = ln_part();
+      LAUNCH(layernorm_backward(dt, dx, mid, G + o.ln1_w, G + o.ln1_b,
+                                l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c,
+                                xin, a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, slot, s,
+                                &md->cols.back()));
+    }
   }
+  LAUNCH(column_reduce_batched(md->cols.data(), (int)md->cols.size(), s));
   // embeddings
   LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
   LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, md->dres, md->B, md->Tn, C, s));
