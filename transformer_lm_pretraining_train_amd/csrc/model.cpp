@@ -154,11 +154,16 @@ struct gpt2_model {
   int32_t* argmax;
   // backward
   // Backward buffers.  Per layer: d res3 (the layer's input gradient from
-  // above), d res2, d fch and d qkv, in two sets used by alternate layers so
-  // that one layer's are still intact while the next is computed (the
-  // weight gradients of two layers run together); dres: d x of the first
-  // layer (the embedding gradient); dbuf_c: scratch activation gradient.
-  void *bw_in[2], *bw_mid[2], *bw_d4[2], *bw_dq[2];
+  // above), d res2, d fch and d qkv, in three sets used in turn (layer l:
+  // set l % 3), so that two layers' are still intact while their weight
+  // gradients run, on the side stream, beside the next layer; dres: d x of
+  // the first layer (the embedding gradient); dbuf_c: scratch activation
+  // gradient.
+  void *bw_in[3], *bw_mid[3], *bw_d4[3], *bw_dq[3];
+  // A second stream for the weight-gradient launches of two layers, which
+  // fill 216 of the 256 CUs: the next layer's work runs beside them.
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> ev_ready, ev_done;  // one pair per two layers
   void *dres, *dbuf_c;
   void* scratch;
   // Column partial sums of every LayerNorm backward and bias gradient of a
@@ -242,7 +247,7 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.ce_lse = (float*)cv.take(M * 4);
   md.argmax = (int32_t*)cv.take(M * 4);
   md.loss_internal = (float*)cv.take(4);
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 3; ++i) {
     md.bw_in[i] = cv.take(M * C * es);
     md.bw_mid[i] = cv.take(M * C * es);
     md.bw_d4[i] = cv.take(M * 4 * C * es);
@@ -302,6 +307,18 @@ int check_launch(hipError_t e, const char* what) {
       ++md->timer_used;                                                             \
     }                                                                               \
   } while (0)
+
+void release_side(gpt2_model* md) {
+  if (md->side) (void)hipStreamSynchronize(md->side);
+  for (hipEvent_t e : md->ev_ready)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : md->ev_done)
+    if (e) (void)hipEventDestroy(e);
+  md->ev_ready.clear();
+  md->ev_done.clear();
+  if (md->side) (void)hipStreamDestroy(md->side);
+  md->side = nullptr;
+}
 
 void release_timer(gpt2_model* md) {
   for (hipEvent_t e : md->timer_ev) (void)hipEventDestroy(e);
@@ -420,13 +437,32 @@ int gpt2_create(const gpt2_config* cfg, void* dev_workspace, size_t bytes, void*
     delete md;
     return fail(GPT2_EHIP, "initialising the workspace: %s", hipGetErrorString(e));
   }
+  // side stream (default priority) and its events: host-side objects only
+  if (md->dt == BF16 && md->L >= 4) {
+    const int np = md->L / 2 + 1;
+    e = hipStreamCreateWithFlags(&md->side, hipStreamNonBlocking);
+    md->ev_ready.assign(np, nullptr);
+    md->ev_done.assign(np, nullptr);
+    for (int i = 0; i < np && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&md->ev_ready[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&md->ev_done[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) {
+      release_side(md);
+      delete md;
+      return fail(GPT2_EHIP, "creating the side stream: %s", hipGetErrorString(e));
+    }
+  }
   *out = md;
   g_err.clear();
   return GPT2_OK;
 }
 
 int gpt2_destroy(gpt2_model* md) {
-  if (md) release_timer(md);
+  if (md) {
+    release_timer(md);
+    release_side(md);
+  }
   delete md;
   return GPT2_OK;
 }
@@ -577,13 +613,25 @@ int gpt2_backward(gpt2_model* md) {
   // are the bias gradient of the linear layer that wrote that residual:
   // fc-proj of the layer below (res3) or proj of the same layer (res2).
   float* fcp_b_below = md->L > 0 ? G + Ly.layers[md->L - 1].fcp_b : nullptr;
-  // Layer l works in buffer set l % 2: in (d res3, from the layer above),
+  // Layer l works in buffer set l % 3: in (d res3, from the layer above),
   // mid (d res2), d4 (d fch), dq (d qkv).  Its four weight gradients are
-  // queued and launched together with the next layer's (one launch of
-  // eight products when their tiles fit the chip in one round, else four at
-  // a time), before that layer's LayerNorm-1 backward overwrites set l % 2.
+  // queued and launched together with the next layer's: one launch of eight
+  // products when their tiles fit the chip in one round (else four at a
+  // time).  Such a pair runs on the side stream, beside the next layer's
+  // work, except the last one; the main stream waits for it before it
+  // writes either of the pair's buffer sets again.
   const int Lh = md->L;
-  void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 2] : md->dres;
+  void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 3] : md->dres;
+  int pend_pair = -1;  // pair running on the side stream whose sets are not yet reusable
+  int pend_sets[2] = {-1, -1};
+  int npairs = 0;
+  auto guard = [&](int set) -> hipError_t {  // main stream: set `set` is about to be written
+    if (pend_pair >= 0 && (pend_sets[0] == set || pend_sets[1] == set)) {
+      pend_pair = -1;
+      return hipStreamWaitEvent(s, md->ev_done[npairs - 1], 0);
+    }
+    return hipSuccess;
+  };
   {
     void* slot = ln_part();
     LAUNCH(layernorm_backward(dt, top, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
@@ -596,10 +644,12 @@ int gpt2_backward(gpt2_model* md) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
     const void* xin = l > 0 ? md->act[l - 1].res3 : md->encoded;
-    void* in = md->bw_in[l % 2];
-    void* mid = md->bw_mid[l % 2];
-    void* d4 = md->bw_d4[l % 2];
-    void* dq = md->bw_dq[l % 2];
+    const int set = l % 3;
+    void* in = md->bw_in[set];
+    void* mid = md->bw_mid[set];
+    void* d4 = md->bw_d4[set];
+    void* dq = md->bw_dq[set];
+    LAUNCH(guard(set));
     // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
     Epilogue e = epi(EPI_GELU_BWD, d4, 4 * C);
     e.aux = a.fch;
@@ -642,7 +692,20 @@ int gpt2_backward(gpt2_model* md) {
     npend += 4;
     if (npend == 8) {
       if (gemm_acc_group_splits(dt, 8, pend, M) > 0) {  // both layers in one round of tiles
-        LAUNCH(gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        if (md->side && l > 1 && npairs < (int)md->ev_done.size()) {
+          // beside the next layer's work: the side stream starts once the
+          // main stream has produced the inputs
+          LAUNCH(hipEventRecord(md->ev_ready[npairs], s));
+          LAUNCH(hipStreamWaitEvent(md->side, md->ev_ready[npairs], 0));
+          LAUNCH(gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, md->side));
+          LAUNCH(hipEventRecord(md->ev_done[npairs], md->side));
+          ++npairs;
+          pend_pair = npairs - 1;
+          pend_sets[0] = (l + 1) % 3;
+          pend_sets[1] = l % 3;
+        } else {
+          LAUNCH(gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        }
         npend = 0;
       } else {  // the layer above alone; this one waits for the next
         LAUNCH(gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
@@ -655,8 +718,9 @@ int gpt2_backward(gpt2_model* md) {
       npend = 0;
     }
     // d x = d res2 + the LayerNorm-1 backward, into the next layer's input
-    // buffer (the other set), or for the first layer the embedding gradient
-    void* dx = l > 0 ? md->bw_in[(l - 1) % 2] : md->dres;
+    // buffer (the next set), or for the first layer the embedding gradient
+    if (l > 0) LAUNCH(guard((l - 1) % 3));
+    void* dx = l > 0 ? md->bw_in[(l - 1) % 3] : md->dres;
     {
       void* slot = ln_part();
       LAUNCH(layernorm_backward(dt, dx, mid, G + o.ln1_w, G + o.ln1_b,
@@ -665,6 +729,8 @@ int gpt2_backward(gpt2_model* md) {
                                 &md->cols.back()));
     }
   }
+  // every weight gradient is in place before the backward returns
+  if (npairs > 0) LAUNCH(hipStreamWaitEvent(s, md->ev_done[npairs - 1], 0));
   LAUNCH(column_reduce_batched(md->cols.data(), (int)md->cols.size(), s));
   // embeddings
   LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
