@@ -483,18 +483,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // out_k[c] += sum_b partial[b * stride + k * C + c] for each non-null out_k
-// (k = 0, 1, 2), summed in a fixed order.  A workgroup covers 16 columns of
-// the concatenated outputs with 4 float4 lanes x 64 groups of partial rows
-// (group g sums rows g, g+64, ...); the 64 group sums are added in order.
-// (16 columns per workgroup: 144-192 workgroups for the GPT-2 widths.)
+// (k = 0, 1, 2), summed in a fixed order.  A workgroup covers 4 Q columns of
+// the concatenated outputs with Q float4 lanes x 256/Q groups of partial
+// rows (group g sums rows g, g + 256/Q, ...); the group sums are added in
+// order.  Q = 4 (16 columns) spreads one reduction over many workgroups;
+// Q = 16 (64 columns, 256-byte row segments) reads more efficiently when
+// many reductions share a launch.
+template <int Q>
 __device__ __forceinline__ void column_reduce_block(const ColReduce& d, int blk) {
-  __shared__ float4 red[64][5];
-  const int q = threadIdx.x % 4, g = threadIdx.x / 4;
-  const int c = blk * 16 + 4 * q;  // first of 4 columns (C % 4 == 0)
+  constexpr int G = 256 / Q;
+  __shared__ float4 red[G][Q + 1];
+  const int q = threadIdx.x % Q, g = threadIdx.x / Q;
+  const int c = blk * 4 * Q + 4 * q;  // first of 4 columns (C % 4 == 0)
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < d.ncols) {
 #pragma unroll 4
-    for (int b = g; b < d.nb; b += 64) {
+    for (int b = g; b < d.nb; b += G) {
       const float4 v = *reinterpret_cast<const float4*>(d.partial + (int64_t)b * d.stride + c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
@@ -503,7 +507,7 @@ __device__ __forceinline__ void column_reduce_block(const ColReduce& d, int blk)
   __syncthreads();
   if (g == 0 && c < d.ncols) {
     float4 t = red[0][q];
-    for (int k = 1; k < 64; ++k) {
+    for (int k = 1; k < G; ++k) {
       const float4 v = red[k][q];
       t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
     }
@@ -519,7 +523,7 @@ __device__ __forceinline__ void column_reduce_block(const ColReduce& d, int blk)
 }
 
 __global__ __launch_bounds__(256) void column_partials_reduce_kernel(const ColReduce d) {
-  column_reduce_block(d, blockIdx.x);
+  column_reduce_block<4>(d, blockIdx.x);
 }
 
 // Several reductions in one launch: descriptor i owns workgroups blk0[i] ..
@@ -533,7 +537,7 @@ struct ColBatch {
 __global__ __launch_bounds__(256) void column_reduce_batch_kernel(const ColBatch cb) {
   int i = 0;
   while (i + 1 < cb.n && (int)blockIdx.x >= cb.blk0[i + 1]) ++i;
-  column_reduce_block(cb.d[i], blockIdx.x - cb.blk0[i]);
+  column_reduce_block<16>(cb.d[i], blockIdx.x - cb.blk0[i]);
 }
 
 static hipError_t column_reduce(const ColReduce& d, hipStream_t s) {
@@ -547,7 +551,7 @@ hipError_t column_reduce_batched(const ColReduce* d, int n, hipStream_t s) {
     cb.n = std::min(kColBatch, n - i0);
     for (int i = 0; i < cb.n; ++i) {
       cb.d[i] = d[i0 + i];
-      cb.blk0[i + 1] = cb.blk0[i] + grid_for(d[i0 + i].ncols, 16);
+      cb.blk0[i + 1] = cb.blk0[i] + grid_for(d[i0 + i].ncols, 64);
     }
     if (cb.blk0[cb.n] > 0) column_reduce_batch_kernel<<<cb.blk0[cb.n], 256, 0, s>>>(cb);
     hipError_t e = hipGetLastError();
