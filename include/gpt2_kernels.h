@@ -50,6 +50,26 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
                void* dev_out2, int64_t ldo2, const void* dev_aux, int64_t ldx, void* dev_ws,
                size_t ws_bytes, void* hip_stream);
 
+/* gpt2k_gemm that also writes per-block column sums of its output, the
+ * first stage of a bias gradient (the bias of a linear layer gets the sum of
+ * the output gradient over all token rows; "Let's reproduce GPT-2 (124M)",
+ * the backward pass of a linear layer):
+ *   colsum[b*ldcs + n] = sum over the rows m in [64b, 64b + 64) ∩ [0, M) of
+ *   the stored out(m, n), as rounded to `dtype`, for b < ceil(M / 64), n < N,
+ * each sum in a fixed order (deterministic).  dev_colsum (fp32, 8-byte
+ * aligned, ldcs even and >= N) may be NULL: then this is gpt2k_gemm.  Only
+ * products for which gpt2k_gemm_colsum_ok() returns 1 can produce the sums
+ * (bf16, GPT2K_EPI_GELU_BWD, a size that runs on the large-tile kernels);
+ * for others a non-NULL dev_colsum returns GPT2_EINVAL and nothing runs. */
+int gpt2k_gemm_colsum_ok(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, int64_t lda,
+                         int64_t ldb, int epilogue);
+int gpt2k_gemm_colsum(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K,
+                      const void* dev_A, int64_t lda, const void* dev_B, int64_t ldb, int epilogue,
+                      void* dev_out, int64_t ldo, const float* dev_bias, const void* dev_resid,
+                      int64_t ldr, void* dev_out2, int64_t ldo2, const void* dev_aux, int64_t ldx,
+                      float* dev_colsum, int64_t ldcs, void* dev_ws, size_t ws_bytes,
+                      void* hip_stream);
+
 /* Weight gradients of up to eight linear layers over the same K tokens:
  * out_i(m, n) += sum_{k < K} A_i[k*lda_i + m] B_i[k*ldb_i + n] for
  * m < M_i, n < N_i, i < n, 1 <= n <= 8 (dW += dy^T x with dy, x stored

@@ -104,3 +104,24 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle/" not in text, f
+
+
+def test_gemm_column_sums_only_where_the_large_tiles_run():
+    """The output column sums (the fc bias gradient's first stage, taken in the
+    GELU-backward product's epilogue) exist for bf16 GELU-backward products that
+    run on the large-tile kernels, and nowhere else; asking for them elsewhere
+    is an error before anything runs."""
+    ok = g.gemm_colsum_ok
+    assert ok(g.GPT2_BF16, True, False, 16384, 3072, 768, 768, 3072, "gelu_bwd")
+    assert ok(g.GPT2_BF16, True, False, 1000, 1001, 200, 200, 1008, "gelu_bwd")
+    assert not ok(g.GPT2_FP32, True, False, 16384, 3072, 768, 768, 3072, "gelu_bwd")
+    assert not ok(g.GPT2_BF16, True, False, 16384, 3072, 768, 768, 3072, "store")
+    assert not ok(g.GPT2_BF16, True, False, 100, 3072, 768, 768, 3072, "gelu_bwd")  # small tiles
+    assert not ok(g.GPT2_BF16, True, False, 16384, 3072, 768, 772, 3072, "gelu_bwd")  # pitch
+    buf = (ctypes.c_float * 64)()
+    rc = g.lib().gpt2k_gemm_colsum(g.GPT2_FP32, 1, 0, 100, 8, 8, ctypes.addressof(buf), 8,
+                                   ctypes.addressof(buf), 8, g.EPI["gelu_bwd"],
+                                   ctypes.addressof(buf), 8, None, None, 0, None, 0,
+                                   ctypes.addressof(buf), 8, ctypes.addressof(buf), 8, None, 0,
+                                   None)
+    assert rc != 0

@@ -187,6 +187,44 @@ def test_gemm_gpt2_124m_shapes_sampled(akm, bkm, M, N, K):
         assert rel_l2(acc[ridx].cpu().numpy(), ref2) < 1e-5
 
 
+@pytest.mark.parametrize("M,N,K,ldo", [(1000, 3072, 768, 3072), (16384, 3072, 768, 3072),
+                                      (520, 1001, 200, 1001)])
+def test_gelu_backward_column_sums(M, N, K, ldo):
+    """The GELU-backward product's column sums per 64-row block (the fc bias
+    gradient's first stage) equal the fp64 sums of the output it stores, and
+    that output is bit-identical to the product's without them: full size,
+    a ragged last row block, and a ragged odd width (element-wise stores)."""
+    rng = np.random.default_rng(M + N)
+    A = bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    B = bf16_round(0.05 * rng.standard_normal((N, K)).astype(np.float32))
+    aux = bf16_round(rng.standard_normal((M, N)).astype(np.float32))
+    Abuf, lda = _store(A, True, M, K, 0, rng, 0.0)
+    Bbuf, ldb = _store(B, False, N, K, 0, rng, 0.0)
+    dA, dB = to_dev(Abuf, torch.bfloat16), to_dev(Bbuf, torch.bfloat16)
+    daux = to_dev(aux, torch.bfloat16)
+    assert g.gemm_colsum_ok(BF16, True, False, M, N, K, lda, ldb, "gelu_bwd")
+    nb, ldcs = (M + 63) // 64, N + N % 2
+    cs = torch.full((nb, ldcs), float("nan"), device="cuda")
+    plain = torch.zeros((M, ldo), dtype=torch.bfloat16, device="cuda")
+    fused = torch.zeros_like(plain)
+    g.gemm(BF16, True, False, M, N, K, dA, lda, dB, ldb, "gelu_bwd", plain, ldo, aux=daux, ldx=N)
+    g.gemm(BF16, True, False, M, N, K, dA, lda, dB, ldb, "gelu_bwd", fused, ldo, aux=daux, ldx=N,
+           colsum=cs, ldcs=ldcs)
+    torch.cuda.synchronize()
+    out = host(fused)[:, :N]
+    assert np.array_equal(out, host(plain)[:, :N])
+    rows = np.zeros((nb * 64, N))
+    rows[:M] = out
+    expect = rows.reshape(nb, 64, N).sum(axis=1)
+    got = host(cs)[:, :N]
+    np.testing.assert_allclose(got, expect, rtol=1e-5, atol=1e-6 * np.abs(out).max())
+    # the output itself: the product's definition on sampled rows
+    idx = rng.choice(M, size=min(M, 64), replace=False)
+    ref = (A[idx].astype(np.float64) @ B.astype(np.float64).T) * oracle.gelu_grad(
+        aux[idx].astype(np.float64))
+    assert rel_l2(out[idx], ref) < 1e-2
+
+
 @pytest.mark.parametrize("M,N", [(768, 3072), (3072, 768), (768, 768), (2304, 768)])
 def test_gemm_weight_gradient_split_k(M, N):
     """The four per-layer weight-gradient products at the 124M shapes

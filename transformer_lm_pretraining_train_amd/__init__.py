@@ -15,8 +15,8 @@ import os
 
 __all__ = [
     "GPT2Config", "TensorInfo", "GPT2Error", "lib", "library_path", "Model", "param_layout",
-    "num_params", "workspace_bytes", "gemm", "gemm_workspace_bytes", "gemm_acc_group",
-    "gemm_acc_group_workspace_bytes", "attention_forward", "attention_backward",
+    "num_params", "workspace_bytes", "gemm", "gemm_colsum_ok", "gemm_workspace_bytes",
+    "gemm_acc_group", "gemm_acc_group_workspace_bytes", "attention_forward", "attention_backward",
     "attention_backward_scratch_bytes", "flops_per_token", "config_for",
     "GPT2_FP32", "GPT2_BF16", "EPI",
 ]
@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "gpt2_last_error": (ctypes.c_char_p, []),
             "gpt2k_gemm": (I, [I, I, I, I, I, I, P, I64, P, I64, I, P, I64, P, P, I64, P, I64, P,
                                I64, P, SZ, P]),
+            "gpt2k_gemm_colsum_ok": (I, [I, I, I, I, I, I, I64, I64, I]),
+            "gpt2k_gemm_colsum": (I, [I, I, I, I, I, I, P, I64, P, I64, I, P, I64, P, P, I64, P,
+                                      I64, P, I64, P, I64, P, SZ, P]),
             "gpt2k_gemm_workspace_bytes": (SZ, [I, I, I, I, I]),
             "gpt2k_gemm_acc_group_workspace_bytes": (SZ, [I, I, P, P, I, P, P]),
             "gpt2k_gemm_acc_group": (I, [I, I, P, P, I, P, P, P, P, P, P, P, SZ, P]),
@@ -273,10 +276,12 @@ def gemm_workspace_bytes(dtype, M, N, K, epilogue):
 
 
 def gemm(dtype, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, epilogue, out, ldo, bias=None,
-         resid=None, ldr=0, out2=None, ldo2=0, aux=None, ldx=0, ws=None, stream=None):
+         resid=None, ldr=0, out2=None, ldo2=0, aux=None, ldx=0, ws=None, stream=None,
+         colsum=None, ldcs=0):
     """C(m, n) = sum_k A(m, k) B(n, k) + epilogue (see gpt2_kernels.h).  For the
     fp32-accumulating epilogue a split-K workspace is allocated here when
-    ``ws`` is None and the product would use one."""
+    ``ws`` is None and the product would use one.  ``colsum`` (fp32, 64-row
+    block column sums of the output) goes to gpt2k_gemm_colsum."""
     epi = EPI[epilogue] if isinstance(epilogue, str) else epilogue
     if ws is None:
         nb = gemm_workspace_bytes(dtype, M, N, K, epi)
@@ -284,9 +289,21 @@ def gemm(dtype, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, epilogue, out, ldo,
             import torch
             ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().gpt2k_gemm(dtype, int(a_kmajor), int(b_kmajor), M, N, K, _ptr(A), lda, _ptr(B),
-                            ldb, epi, _ptr(out), ldo, _ptr(bias), _ptr(resid), ldr, _ptr(out2),
-                            ldo2, _ptr(aux), ldx, _ptr(ws), nbytes, _stream(stream)))
+    if colsum is None:
+        _check(lib().gpt2k_gemm(dtype, int(a_kmajor), int(b_kmajor), M, N, K, _ptr(A), lda, _ptr(B),
+                                ldb, epi, _ptr(out), ldo, _ptr(bias), _ptr(resid), ldr, _ptr(out2),
+                                ldo2, _ptr(aux), ldx, _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check(lib().gpt2k_gemm_colsum(dtype, int(a_kmajor), int(b_kmajor), M, N, K, _ptr(A), lda,
+                                       _ptr(B), ldb, epi, _ptr(out), ldo, _ptr(bias), _ptr(resid),
+                                       ldr, _ptr(out2), ldo2, _ptr(aux), ldx, _ptr(colsum), ldcs,
+                                       _ptr(ws), nbytes, _stream(stream)))
+
+
+def gemm_colsum_ok(dtype, a_kmajor, b_kmajor, M, N, K, lda, ldb, epilogue):
+    epi = EPI[epilogue] if isinstance(epilogue, str) else epilogue
+    return bool(lib().gpt2k_gemm_colsum_ok(dtype, int(a_kmajor), int(b_kmajor), M, N, K, lda, ldb,
+                                           epi))
 
 
 def _arr(ctype, vals):

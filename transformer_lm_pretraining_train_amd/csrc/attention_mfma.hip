@@ -167,7 +167,9 @@ __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x
 // exact.
 constexpr float RESCALE_LOG2 = 8.0f;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_mfma(
+// The forward and dQ kernels fit in 168 registers: three workgroups (12
+// waves) per CU.  The dK/dV kernel needs more and runs two.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_fwd_mfma(
     bf16* __restrict__ out, float* __restrict__ lse, const bf16* __restrict__ qkv, int T, int H,
     int nqb) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // --------------------------------------------------------------- backward: dQ
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_bwd_dq_mfma(bf16* __restrict__ dqkv, float* __restrict__ Dbuf,
                                                         const bf16* __restrict__ dout,
                                                         const bf16* __restrict__ qkv,
                                                         const bf16* __restrict__ out,

@@ -30,29 +30,32 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- epilogue
+// Returns the value stored to out[m, n] (as rounded to T; 0 for EPI_ACC_F32).
 template <int MODE, class T>
-__device__ __forceinline__ void epi_apply(const Epilogue& e, int m, int n, float acc) {
+__device__ __forceinline__ float epi_apply(const Epilogue& e, int m, int n, float acc) {
+  T y;
   if constexpr (MODE == EPI_STORE) {
-    ((T*)e.out)[(int64_t)m * e.ldo + n] = from_f<T>(acc);
+    y = from_f<T>(acc);
   } else if constexpr (MODE == EPI_BIAS) {
-    ((T*)e.out)[(int64_t)m * e.ldo + n] = from_f<T>(acc + e.bias[n]);
+    y = from_f<T>(acc + e.bias[n]);
   } else if constexpr (MODE == EPI_BIAS_RESID) {
     float r = to_f(((const T*)e.resid)[(int64_t)m * e.ldr + n]);
-    ((T*)e.out)[(int64_t)m * e.ldo + n] = from_f<T>(acc + e.bias[n] + r);
+    y = from_f<T>(acc + e.bias[n] + r);
   } else if constexpr (MODE == EPI_BIAS_GELU) {
-    float h = acc + e.bias[n];
-    T hq = from_f<T>(h);
-    ((T*)e.out)[(int64_t)m * e.ldo + n] = hq;
+    y = from_f<T>(acc + e.bias[n]);
     // GELU of the stored (rounded) pre-activation, so that the backward,
     // which differentiates at the stored value, is consistent with it.
-    ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(to_f(hq)));
+    ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(to_f(y)));
   } else if constexpr (MODE == EPI_GELU_BWD) {
     float h = to_f(((const T*)e.aux)[(int64_t)m * e.ldx + n]);
-    ((T*)e.out)[(int64_t)m * e.ldo + n] = from_f<T>(acc * gelu_grad_f(h));
+    y = from_f<T>(acc * gelu_grad_f(h));
   } else {  // EPI_ACC_F32
-    float* o = (float*)e.out + (int64_t)m * e.ldo + n;
-    *o += acc;
+    float* of = (float*)e.out + (int64_t)m * e.ldo + n;
+    *of += acc;
+    return 0.f;
   }
+  ((T*)e.out)[(int64_t)m * e.ldo + n] = y;
+  return to_f(y);
 }
 
 // ================================================================ fp32 SIMT
@@ -262,9 +265,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K,
 // to out + split * M * N and splitk_reduce adds them in order.
 // Epilogue on 8 consecutive columns n .. n+7 of row m (16-byte accesses when
 // the row pitches allow it, element-wise at the ragged right edge).
+// res[j]: the value stored to out[m, n + j] as rounded (bf16 outputs; 0
+// past N).
 template <int MODE>
 __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int N, const float* v,
-                                           int split, int M) {
+                                           int split, int M, float* res) {
   if constexpr (MODE == EPI_PARTIAL) {
     float* o = (float*)e.out + (int64_t)split * M * N + (int64_t)m * N + n;
     if (n + 8 <= N && (N & 3) == 0) {
@@ -278,7 +283,7 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
     const bool vec = n + 8 <= N && (e.ldo & 7) == 0 && (e.ldr & 7) == 0 && (e.ldo2 & 7) == 0 &&
                      (e.ldx & 7) == 0;
     if (!vec) {
-      for (int j = 0; j < 8 && n + j < N; ++j) epi_apply<MODE, bf16>(e, m, n + j, v[j]);
+      for (int j = 0; j < 8; ++j) res[j] = n + j < N ? epi_apply<MODE, bf16>(e, m, n + j, v[j]) : 0.f;
       return;
     }
     if constexpr (MODE == EPI_ACC_F32) {
@@ -311,6 +316,8 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
       Pack<bf16> o;
 #pragma unroll
       for (int j = 0; j < 8; ++j) o.e[j] = (bf16)x[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) res[j] = to_f(o.e[j]);
       store_pack((bf16*)e.out + (int64_t)m * e.ldo + n, o);
       if constexpr (MODE == EPI_BIAS_GELU) {
         Pack<bf16> g2;
@@ -634,6 +641,16 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
   // waves 0 .. NW/2-1 stage in the first operand buffer, the others in the second
   static_assert((NW / 2) * 32 * SP * 4 <= SM::STAGE * 2, "epilogue staging exceeds LDS");
   float* slab = reinterpret_cast<float*>(wave < NW / 2 ? smem0 : smem1) + (wave % (NW / 2)) * 32 * SP;
+  // Column sums of the output (Epilogue::colsum): the stored values go back
+  // into the slab, and lane c < 16 JB sums slab columns 2c, 2c+1 over the
+  // 32 rows, then over the wave's TI row blocks -- the wave's WM = 64 rows,
+  // one colsum block.
+  constexpr bool kColsum = MODE == EPI_GELU_BWD;
+  static_assert(!kColsum || WM == 64, "colsum blocks are the waves' 64 rows");
+  const bool colsum = kColsum && e.colsum != nullptr;
+  float2 csum[TJ / JB];
+#pragma unroll
+  for (int jr = 0; jr < TJ / JB; ++jr) csum[jr] = make_float2(0.f, 0.f);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
@@ -659,9 +676,41 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         const float4 b = *reinterpret_cast<const float4*>(slab + row * SP + col + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const int m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + jr * JB * 32 + col;
-        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, split, M);
+        float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, split, M, res);
+        if (colsum) {  // this lane alone read these slab entries
+          *reinterpret_cast<float4*>(slab + row * SP + col) = make_float4(res[0], res[1], res[2], res[3]);
+          *reinterpret_cast<float4*>(slab + row * SP + col + 4) = make_float4(res[4], res[5], res[6], res[7]);
+        }
       }
       __builtin_amdgcn_wave_barrier();
+      if (colsum && lane < 16 * JB) {
+        float2 t = make_float2(0.f, 0.f);
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) {
+          const float2 x = *reinterpret_cast<const float2*>(slab + r * SP + 2 * lane);
+          t.x += x.x;
+          t.y += x.y;
+        }
+        csum[jr].x += t.x;
+        csum[jr].y += t.y;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if (colsum && lane < 16 * JB) {
+    const int blk = (m0 + wm * WM) / 64;
+    if (m0 + wm * WM < M) {
+#pragma unroll
+      for (int jr = 0; jr < TJ / JB; ++jr) {
+        const int n = n0 + wn * WN + jr * JB * 32 + 2 * lane;
+        float* cp = e.colsum + (int64_t)blk * e.ldcs + n;
+        if (n + 1 < N) {
+          *reinterpret_cast<float2*>(cp) = csum[jr];
+        } else if (n < N) {
+          cp[0] = csum[jr].x;
+        }
+      }
     }
   }
   __syncthreads();  // the next tile's loads overwrite the staging slabs
@@ -972,9 +1021,24 @@ size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode) {
   return (size_t)p.splits * M * N * sizeof(float);
 }
 
+// The column sums come from the large-tile kernels' epilogue only: bf16,
+// GELU backward, and a plan and operand spans that select those kernels.
+bool gemm_colsum_ok(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, int64_t lda,
+                    int64_t ldb, int mode) {
+  if (dt != BF16 || mode != EPI_GELU_BWD || M <= 0 || N <= 0 || lda % 8 || ldb % 8) return false;
+  const Plan p = plan_gemm(M, N, K, mode);
+  return p.kind != 0 && operand_span(a_kmajor, M, K, lda) < (int64_t(1) << 31) &&
+         operand_span(b_kmajor, N, K, ldb) < (int64_t(1) << 31);
+}
+
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
                 void* ws, size_t ws_bytes) {
+  if (e.colsum) {
+    if (!gemm_colsum_ok(dt, a_kmajor, b_kmajor, M, N, K, lda, ldb, e.mode)) return hipErrorNotSupported;
+    if (e.ldcs < N || e.ldcs % 2 != 0 || reinterpret_cast<uintptr_t>(e.colsum) % 8 != 0)
+      return hipErrorInvalidValue;
+  }
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dt == BF16 && (lda % 8 != 0 || ldb % 8 != 0)) return hipErrorInvalidValue;
   if (const int r = acc_row_split(dt, M, N, K, e.mode)) {

@@ -103,6 +103,13 @@ struct Epilogue {
   int64_t ldo2;
   const void* aux;
   int64_t ldx;
+  // EPI_GELU_BWD only, and only where gemm_colsum_ok(): if not null, also
+  // colsum[b * ldcs + n] = sum of the stored out[m, n] (as rounded) over the
+  // 64 rows m of block b, for b < gemm_colsum_blocks(M) and n < N: per-block
+  // column sums of the output (a bias gradient's first stage), in a fixed
+  // order.
+  float* colsum;
+  int64_t ldcs;
 };
 // Split-K (used for fp32-accumulating products with few output tiles and a
 // long K) needs gemm_workspace_bytes() of scratch in `ws`.
@@ -110,6 +117,12 @@ size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode);
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
                 void* ws = nullptr, size_t ws_bytes = 0);
+// Whether gemm() can produce Epilogue::colsum for this product (it returns
+// hipErrorNotSupported for a colsum it cannot produce), and the number of
+// 64-row blocks it then writes.
+bool gemm_colsum_ok(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, int64_t lda,
+                    int64_t ldb, int mode);
+inline int gemm_colsum_blocks(int M) { return (M + 63) / 64; }
 // out (fp32, pitch ldo) += sum_k A[k * lda + m] B[k * ldb + n] for m < M,
 // n < N: a weight gradient dW += dy^T x with dy and x stored row-major.
 struct AccItem {

@@ -25,6 +25,25 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
                int64_t lda, const void* B, int64_t ldb, int epilogue, void* out, int64_t ldo,
                const float* bias, const void* resid, int64_t ldr, void* out2, int64_t ldo2,
                const void* aux, int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
+  return gpt2k_gemm_colsum(dtype, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, epilogue, out, ldo,
+                           bias, resid, ldr, out2, ldo2, aux, ldx, nullptr, 0, ws, ws_bytes,
+                           stream);
+}
+
+int gpt2k_gemm_colsum_ok(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, int64_t lda,
+                         int64_t ldb, int epilogue) {
+  return gemm_colsum_ok(dtype, a_kmajor != 0, b_kmajor != 0, M, N, K, lda, ldb, epilogue) ? 1 : 0;
+}
+
+int gpt2k_gemm_colsum(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const void* A,
+                      int64_t lda, const void* B, int64_t ldb, int epilogue, void* out,
+                      int64_t ldo, const float* bias, const void* resid, int64_t ldr, void* out2,
+                      int64_t ldo2, const void* aux, int64_t ldx, float* colsum, int64_t ldcs,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (colsum && !gemm_colsum_ok(dtype, a_kmajor != 0, b_kmajor != 0, M, N, K, lda, ldb, epilogue))
+    return gpt2_internal_fail(GPT2_EINVAL, "column sums not available for this product");
+  if (colsum && (ldcs < N || ldcs % 2 || reinterpret_cast<uintptr_t>(colsum) % 8))
+    return gpt2_internal_fail(GPT2_EINVAL, "ldcs must be even and >= N, colsum 8-byte aligned");
   if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
     return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
   if (M < 0 || N < 0 || K < 0 || !A || !B || !out)
@@ -48,6 +67,8 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
   e.ldo2 = ldo2;
   e.aux = aux;
   e.ldx = ldx;
+  e.colsum = colsum;
+  e.ldcs = ldcs;
   return launch_rc(gemm(dtype, a_kmajor != 0, b_kmajor != 0, M, N, K, A, lda, B, ldb, e,
                         (hipStream_t)stream, ws, ws_bytes),
                    "gemm");

@@ -261,7 +261,9 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   sc = std::max(sc, encoder_backward_wte_scratch_bytes((int)M, c.vocab_size, (int)C));
   md.scratch = cv.take(sc);
   md.ln_slot = (layernorm_backward_scratch_bytes((int)M, (int)C) + kAlign - 1) / kAlign * kAlign;
-  md.bg_slot = (bias_grad_scratch_bytes((int)M, (int)(4 * C)) + kAlign - 1) / kAlign * kAlign;
+  md.bg_slot = std::max(bias_grad_scratch_bytes((int)M, (int)(4 * C)),
+                        (size_t)gemm_colsum_blocks((int)M) * 4 * C * sizeof(float));
+  md.bg_slot = (md.bg_slot + kAlign - 1) / kAlign * kAlign;
   md.colpart = cv.take((size_t)(2 * c.n_layer + 1) * md.ln_slot + (size_t)(2 * c.n_layer) * md.bg_slot);
   md.cols.reserve(4 * c.n_layer + 1);
   size_t gw = 0;
@@ -654,12 +656,21 @@ int gpt2_backward(gpt2_model* md) {
     Epilogue e = epi(EPI_GELU_BWD, d4, 4 * C);
     e.aux = a.fch;
     e.ldx = 4 * C;
+    // d fc_b = column sums of d4: per 64-row block in the product's epilogue
+    // where it can, else a pass over d4 after the next product
+    const bool fcb_fused = gemm_colsum_ok(dt, true, false, M, 4 * C, C, C, 4 * C, EPI_GELU_BWD);
+    if (fcb_fused) {
+      float* slot = (float*)bg_part();
+      e.colsum = slot;
+      e.ldcs = 4 * C;
+      md->cols.back() = ColReduce{G + o.fc_b, nullptr, nullptr, slot, gemm_colsum_blocks(M),
+                                  4 * C, 4 * C, 4 * C};
+    }
     LAUNCH(gemm(dt, true, false, M, 4 * C, C, in, C, md->wt(o.fcp_w), 4 * C, e, s));
-    // fc: fch = ln2 fc_w^T + fc_b  (d4 holds d fch; its column sums are taken
-    // right after the product that reads it)
+    // fc: fch = ln2 fc_w^T + fc_b  (d4 holds d fch)
     LAUNCH(gemm(dt, true, false, M, C, 4 * C, d4, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    {
+    if (!fcb_fused) {
       void* slot = bg_part();
       LAUNCH(bias_grad(dt, G + o.fc_b, d4, M, 4 * C, 4 * C, slot, s, &md->cols.back()));
     }
