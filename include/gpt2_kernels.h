@@ -105,6 +105,23 @@ int gpt2k_attention_backward(int dtype, void* dev_dqkv, const void* dev_dout, co
                              const void* dev_out, const float* dev_lse, int B, int T, int H,
                              int hd, void* dev_scratch, void* hip_stream);
 
+/* gpt2k_attention_backward that also writes per-block column sums of dqkv,
+ * the first stage of the qkv bias gradient (sum of d qkv over all token
+ * rows; "Let's reproduce GPT-2 (124M)", the backward pass of the qkv linear
+ * layer):
+ *   dev_colsum[(b*ceil(T/128) + i)*3C + c] = sum over t in
+ *   [128i, 128i + 128) ∩ [0, T) of the stored dqkv(b*T + t, c)
+ * (as rounded to `dtype`; fp32 sums in a fixed order), for every b < B,
+ * i < ceil(T/128), c < 3C.  dev_colsum may be NULL (then this is
+ * gpt2k_attention_backward); where gpt2k_attention_colsum_ok(dtype, hd) is 0
+ * (only bf16 with hd = 64 has them) a non-NULL dev_colsum returns
+ * GPT2_EINVAL before anything runs. */
+int gpt2k_attention_colsum_ok(int dtype, int hd);
+int gpt2k_attention_backward_colsum(int dtype, void* dev_dqkv, const void* dev_dout,
+                                    const void* dev_qkv, const void* dev_out,
+                                    const float* dev_lse, int B, int T, int H, int hd,
+                                    void* dev_scratch, float* dev_colsum, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

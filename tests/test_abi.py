@@ -125,3 +125,17 @@ def test_gemm_column_sums_only_where_the_large_tiles_run():
                                    ctypes.addressof(buf), 8, ctypes.addressof(buf), 8, None, 0,
                                    None)
     assert rc != 0
+
+
+def test_attention_column_sums_only_on_the_matrix_core_path():
+    """The qkv bias gradient's column sums come from the bf16, head-size-64
+    attention backward only; elsewhere asking for them is an error before
+    anything runs."""
+    assert g.attention_colsum_ok(g.GPT2_BF16, 64)
+    assert not g.attention_colsum_ok(g.GPT2_FP32, 64)
+    assert not g.attention_colsum_ok(g.GPT2_BF16, 32)
+    buf = (ctypes.c_float * 64)()
+    p = ctypes.addressof(buf)
+    rc = g.lib().gpt2k_attention_backward_colsum(g.GPT2_FP32, p, p, p, p, p, 1, 4, 1, 16, p, p,
+                                                 None)
+    assert rc != 0

@@ -387,3 +387,35 @@ def test_attention_gpt2_124m_sampled_heads():
         for part in range(3):
             sl = slice(part * hd, (part + 1) * hd)
             assert cosine(got[:, sl], rd[:, sl]) > 0.999
+
+
+@pytest.mark.parametrize("B,T,H", [(2, 100, 3), (1, 300, 2), (16, 1024, 12)])
+def test_attention_backward_column_sums(B, T, H):
+    """The attention backward's column sums of dqkv per 128-row block (the qkv
+    bias gradient's first stage) equal the fp64 sums of the dqkv it stores,
+    and that dqkv is bit-identical to the backward's without them: ragged T
+    (a partial last block, T below one block) and the GPT-2 124M shape."""
+    hd, C = 64, H * 64
+    assert g.attention_colsum_ok(BF16, hd)
+    rng = np.random.default_rng(B * T + H)
+    qkv = bf16_round(rng.standard_normal((B * T, 3 * C)).astype(np.float32))
+    dout = bf16_round(rng.standard_normal((B * T, C)).astype(np.float32))
+    d_qkv, d_dout = to_dev(qkv, torch.bfloat16), to_dev(dout, torch.bfloat16)
+    d_out = torch.empty((B * T, C), dtype=torch.bfloat16, device="cuda")
+    d_lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    g.attention_forward(BF16, d_out, d_lse, d_qkv, B, T, H, hd)
+    scratch = torch.empty(g.attention_backward_scratch_bytes(B, T, H), dtype=torch.uint8,
+                          device="cuda")
+    nblk = (T + 127) // 128
+    cs = torch.full((B * nblk, 3 * C), float("nan"), device="cuda")
+    plain = torch.full((B * T, 3 * C), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fused = torch.full_like(plain, float("nan"))
+    g.attention_backward(BF16, plain, d_dout, d_qkv, d_out, d_lse, B, T, H, hd, scratch)
+    g.attention_backward(BF16, fused, d_dout, d_qkv, d_out, d_lse, B, T, H, hd, scratch, colsum=cs)
+    torch.cuda.synchronize()
+    got_dqkv = host(fused)
+    assert np.array_equal(got_dqkv, host(plain))
+    rows = np.zeros((B, nblk * 128, 3 * C))
+    rows[:, :T] = got_dqkv.reshape(B, T, 3 * C)
+    expect = rows.reshape(B * nblk, 128, 3 * C).sum(axis=1)
+    np.testing.assert_allclose(host(cs), expect, rtol=1e-5, atol=1e-6 * np.abs(got_dqkv).max())

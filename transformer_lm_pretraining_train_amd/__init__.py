@@ -17,6 +17,7 @@ __all__ = [
     "GPT2Config", "TensorInfo", "GPT2Error", "lib", "library_path", "Model", "param_layout",
     "num_params", "workspace_bytes", "gemm", "gemm_colsum_ok", "gemm_workspace_bytes",
     "gemm_acc_group", "gemm_acc_group_workspace_bytes", "attention_forward", "attention_backward",
+    "attention_colsum_ok",
     "attention_backward_scratch_bytes", "flops_per_token", "config_for",
     "GPT2_FP32", "GPT2_BF16", "EPI",
 ]
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
             "gpt2k_attention_forward": (I, [I, P, P, P, I, I, I, I, P]),
             "gpt2k_attention_backward_scratch_bytes": (SZ, [I, I, I]),
             "gpt2k_attention_backward": (I, [I, P, P, P, P, P, I, I, I, I, P, P]),
+            "gpt2k_attention_colsum_ok": (I, [I, I]),
+            "gpt2k_attention_backward_colsum": (I, [I, P, P, P, P, P, I, I, I, I, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -348,6 +351,14 @@ def attention_backward_scratch_bytes(B, T, H):
     return lib().gpt2k_attention_backward_scratch_bytes(B, T, H)
 
 
-def attention_backward(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, scratch, stream=None):
-    _check(lib().gpt2k_attention_backward(dtype, _ptr(dqkv), _ptr(dout), _ptr(qkv), _ptr(out),
-                                          _ptr(lse), B, T, H, hd, _ptr(scratch), _stream(stream)))
+def attention_backward(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, scratch, stream=None,
+                       colsum=None):
+    """``colsum``: fp32 (B * ceil(T/128), 3C) column sums of dqkv per 128-row
+    block (gpt2k_attention_backward_colsum)."""
+    _check(lib().gpt2k_attention_backward_colsum(dtype, _ptr(dqkv), _ptr(dout), _ptr(qkv),
+                                                 _ptr(out), _ptr(lse), B, T, H, hd,
+                                                 _ptr(scratch), _ptr(colsum), _stream(stream)))
+
+
+def attention_colsum_ok(dtype, hd):
+    return bool(lib().gpt2k_attention_colsum_ok(dtype, hd))

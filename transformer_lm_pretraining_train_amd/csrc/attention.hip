@@ -23,7 +23,7 @@ hipError_t attention_forward_mfma(void* out, float* lse, const void* qkv, int B,
                                   hipStream_t s);
 hipError_t attention_backward_mfma(void* dqkv, const void* dout, const void* qkv, const void* out,
                                    const float* lse, float* Dbuf, int B, int T, int H,
-                                   hipStream_t s);
+                                   hipStream_t s, float* colsum);
 
 constexpr int AT_TILE = 64;
 
@@ -301,12 +301,15 @@ size_t attention_backward_scratch_bytes(int B, int T, int H) {
   return (size_t)B * H * T * sizeof(float);
 }
 
+bool attention_colsum_ok(int dt, int hd) { return attention_mfma_supported(dt, hd); }
+
 hipError_t attention_backward(int dt, void* dqkv, const void* dout, const void* qkv,
                               const void* out, const float* lse, int B, int Tn, int H, int hd,
-                              void* scratch, hipStream_t s) {
+                              void* scratch, hipStream_t s, float* colsum) {
   float* Dbuf = (float*)scratch;
   if (attention_mfma_supported(dt, hd))
-    return attention_backward_mfma(dqkv, dout, qkv, out, lse, Dbuf, B, Tn, H, s);
+    return attention_backward_mfma(dqkv, dout, qkv, out, lse, Dbuf, B, Tn, H, s, colsum);
+  if (colsum) return hipErrorNotSupported;
   if (dt == BF16) {
     using T = bf16;
     AT_DISPATCH_HD(hd, launch_bwd, dqkv, Dbuf, dout, qkv, out, lse, B, Tn, H, s);

@@ -154,6 +154,33 @@ __device__ __forceinline__ void store_acc_row(bf16* __restrict__ dst, const f32x
   }
 }
 
+// Column sums of a workgroup's 128 stored rows x 64 columns (the first stage
+// of the qkv bias gradient): each lane puts its row's 32 values of `a` (as
+// stored: bf16 of a * mul, 0 for an invalid row) into LDS, then lane c of
+// the first wave adds column c over the 128 rows in order.  Call after the
+// workgroup's last barrier-ended tile (the staging LDS is free), by all
+// threads.
+__device__ __forceinline__ void colsum_rows128(float* __restrict__ dst, const f32x16_t (&a)[2],
+                                               float mul, bool valid, bf16* smem, int wave,
+                                               int l32, int h2) {
+  constexpr int P = HD + 1;  // row pitch (floats)
+  static_assert(128 * P * 4 <= 4 * TILE * 2, "column-sum staging exceeds the LDS tiles");
+  float* red = reinterpret_cast<float*>(smem);
+  const int row = wave * 32 + l32;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      red[row * P + dt * 32 + acc_row(r, h2)] = valid ? (float)(bf16)(a[dt][r] * mul) : 0.f;
+  __syncthreads();
+  if (threadIdx.x < HD) {
+    float t = 0.f;
+    for (int i = 0; i < 128; ++i) t += red[i * P + threadIdx.x];
+    dst[threadIdx.x] = t;
+  }
+  __syncthreads();
+}
+
 // --------------------------------------------------------------- forward
 // Online softmax with a lazily moved reference: each query keeps a running
 // reference m (log2 units) and accumulates l = sum exp2(s c - m) and
@@ -323,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                                         const bf16* __restrict__ qkv,
                                                         const bf16* __restrict__ out,
                                                         const float* __restrict__ lse, int T, int H,
-                                                        int nqb) {
+                                                        int nqb, float* __restrict__ colsum) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
   const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
@@ -426,6 +453,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) store_acc_row(dst, dq[dt], 0.125f, dt * 32, h2);
   }
+  if (colsum)
+    colsum_rows128(colsum + (int64_t)(b * nqb + qb) * ld + hh * HD, dq, 0.125f, qvalid, smem, wave,
+                   l32, h2);
 }
 
 // --------------------------------------------------------------- backward: dK, dV
@@ -433,7 +463,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                          const float* __restrict__ Dbuf,
                                                          const bf16* __restrict__ dout,
                                                          const bf16* __restrict__ qkv,
-                                                         const float* __restrict__ lse, int T, int H) {
+                                                         const float* __restrict__ lse, int T, int H,
+                                                         float* __restrict__ colsum) {
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][Q | dO]
   __shared__ __attribute__((aligned(16))) float LD[2][2][TB];   // [stage][L | D]
   const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
@@ -547,6 +578,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       store_acc_row(dst + 2 * C, dv[dt], 1.0f, dt * 32, h2);
     }
   }
+  if (colsum) {
+    float* cs = colsum + (int64_t)(b * nkb_total + kblk) * ld + hh * HD;
+    colsum_rows128(cs + C, dk, 0.125f, kvalid, smem, wave, l32, h2);
+    colsum_rows128(cs + 2 * C, dv, 1.0f, kvalid, smem, wave, l32, h2);
+  }
 }
 
 }  // namespace
@@ -563,13 +599,14 @@ hipError_t attention_forward_mfma(void* out, float* lse, const void* qkv, int B,
 
 hipError_t attention_backward_mfma(void* dqkv, const void* dout, const void* qkv, const void* out,
                                    const float* lse, float* Dbuf, int B, int T, int H,
-                                   hipStream_t s) {
+                                   hipStream_t s, float* colsum) {
   const int nb = (int)cdiv(T, WQ);
+  static_assert(WQ == 128, "column-sum blocks are the workgroups' 128 rows");
   dim3 grid((unsigned)(nb * B * H));
   attn_bwd_dq_mfma<<<grid, 256, 0, s>>>((bf16*)dqkv, Dbuf, (const bf16*)dout, (const bf16*)qkv,
-                                        (const bf16*)out, lse, T, H, nb);
+                                        (const bf16*)out, lse, T, H, nb, colsum);
   attn_bwd_dkv_mfma<<<grid, 256, 0, s>>>((bf16*)dqkv, Dbuf, (const bf16*)dout, (const bf16*)qkv,
-                                         lse, T, H);
+                                         lse, T, H, colsum);
   return hipGetLastError();
 }
 

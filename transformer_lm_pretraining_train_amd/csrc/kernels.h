@@ -72,11 +72,17 @@ hipError_t crossentropy_fused(int dt, float* losses, float* lse, int32_t* argmax
 // ---- attention (qkv rows of 3C: [q | k | v], head h at h*hd)
 hipError_t attention_forward(int dt, void* out, float* lse, const void* qkv, int B, int T, int H,
                              int hd, hipStream_t s);
-// dqkv fully written.  scratch: attention_backward_scratch_bytes.
+// dqkv fully written.  scratch: attention_backward_scratch_bytes.  colsum
+// (where attention_colsum_ok(), else hipErrorNotSupported; may be null):
+// colsum[(b * ceil(T/128) + i) * 3C + c] = sum of the stored dqkv[b*T + t, c]
+// over t in [128 i, 128 i + 128) ∩ [0, T), for all 3C columns, in a fixed
+// order (the qkv bias gradient's first stage).
 size_t attention_backward_scratch_bytes(int B, int T, int H);
+bool attention_colsum_ok(int dt, int hd);
+inline int attention_colsum_blocks(int B, int T) { return B * ((T + 127) / 128); }
 hipError_t attention_backward(int dt, void* dqkv, const void* dout, const void* qkv,
                               const void* out, const float* lse, int B, int T, int H, int hd,
-                              void* scratch, hipStream_t s);
+                              void* scratch, hipStream_t s, float* colsum = nullptr);
 
 // ---- GEMM: C(m, n) = sum_k A(m, k) B(n, k), then an epilogue.
 // a_kmajor: A(m,k) = A[m*lda + k], else A[k*lda + m]; likewise b_kmajor for

@@ -134,6 +134,17 @@ size_t gpt2k_attention_backward_scratch_bytes(int B, int T, int H) {
 int gpt2k_attention_backward(int dtype, void* dqkv, const void* dout, const void* qkv,
                              const void* out, const float* lse, int B, int T, int H, int hd,
                              void* scratch, void* stream) {
+  return gpt2k_attention_backward_colsum(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, scratch,
+                                         nullptr, stream);
+}
+
+int gpt2k_attention_colsum_ok(int dtype, int hd) { return attention_colsum_ok(dtype, hd) ? 1 : 0; }
+
+int gpt2k_attention_backward_colsum(int dtype, void* dqkv, const void* dout, const void* qkv,
+                                    const void* out, const float* lse, int B, int T, int H, int hd,
+                                    void* scratch, float* colsum, void* stream) {
+  if (colsum && !attention_colsum_ok(dtype, hd))
+    return gpt2_internal_fail(GPT2_EINVAL, "column sums not available for this dtype / head size");
   if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
     return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
   if (!dqkv || !dout || !qkv || !out || !lse || !scratch || B < 1 || T < 1 || H < 1)
@@ -141,7 +152,7 @@ int gpt2k_attention_backward(int dtype, void* dqkv, const void* dout, const void
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
     return gpt2_internal_fail(GPT2_EINVAL, "head size must be 16, 32, 64 or 128");
   return launch_rc(attention_backward(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, scratch,
-                                      (hipStream_t)stream),
+                                      (hipStream_t)stream, colsum),
                    "attention_backward");
 }
 

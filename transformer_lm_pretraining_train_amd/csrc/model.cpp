@@ -261,8 +261,10 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   sc = std::max(sc, encoder_backward_wte_scratch_bytes((int)M, c.vocab_size, (int)C));
   md.scratch = cv.take(sc);
   md.ln_slot = (layernorm_backward_scratch_bytes((int)M, (int)C) + kAlign - 1) / kAlign * kAlign;
-  md.bg_slot = std::max(bias_grad_scratch_bytes((int)M, (int)(4 * C)),
-                        (size_t)gemm_colsum_blocks((int)M) * 4 * C * sizeof(float));
+  md.bg_slot = std::max({bias_grad_scratch_bytes((int)M, (int)(4 * C)),
+                         (size_t)gemm_colsum_blocks((int)M) * 4 * C * sizeof(float),
+                         (size_t)attention_colsum_blocks(c.micro_batch, c.seq_len) * 3 * C *
+                             sizeof(float)});
   md.bg_slot = (md.bg_slot + kAlign - 1) / kAlign * kAlign;
   md.colpart = cv.take((size_t)(2 * c.n_layer + 1) * md.ln_slot + (size_t)(2 * c.n_layer) * md.bg_slot);
   md.cols.reserve(4 * c.n_layer + 1);
@@ -684,12 +686,21 @@ int gpt2_backward(gpt2_model* md) {
     // attention output projection: res2 = x + atty proj_w^T + proj_b
     LAUNCH(gemm(dt, true, false, M, C, C, mid, C, md->wt(o.proj_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
+    // d qkv_b = column sums of dq: per 128-row block in the attention
+    // backward where it can, else a pass over dq after the next product
+    float* qkvb_part = nullptr;
+    if (attention_colsum_ok(dt, md->hd)) {
+      qkvb_part = (float*)bg_part();
+      md->cols.back() = ColReduce{G + o.qkv_b, nullptr, nullptr, qkvb_part,
+                                  attention_colsum_blocks(md->B, md->Tn), 3 * C, 3 * C, 3 * C};
+    }
     TIMED(GPT2_TIMER_ATTN_BWD, attention_backward(dt, dq, md->dbuf_c, a.qkv, a.atty, a.lse,
-                                                  md->B, md->Tn, H, md->hd, md->scratch, s));
+                                                  md->B, md->Tn, H, md->hd, md->scratch, s,
+                                                  qkvb_part));
     // qkv = ln1 qkv_w^T + qkv_b
     LAUNCH(gemm(dt, true, false, M, C, 3 * C, dq, 3 * C, md->wt(o.qkv_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
-    {
+    if (!qkvb_part) {
       void* slot = bg_part();
       LAUNCH(bias_grad(dt, G + o.qkv_b, dq, M, 3 * C, 3 * C, slot, s, &md->cols.back()));
     }
