@@ -362,3 +362,24 @@ def test_gradients_bitwise_repeatable():
             m.backward()
         grads.append(host(m.get_grads()))
     assert np.array_equal(grads[0], grads[1])
+
+
+def test_bf16_width_768_long_token_runs_match_oracle():
+    """The token-embedding gradient when one token fills most positions: its
+    run of sorted positions spans many 32-slot windows (and both column
+    groups of a 768-wide row), so the ordered partial sums of runs that
+    cross windows carry most of its row."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "bf16", B=2, n_layer=1,
+                                                      n_embd=768, n_head=12)
+    rng = np.random.default_rng(5)
+    x, y = batches[0]
+    x = np.where(rng.random(x.shape) < 0.8, 3, x).astype(x.dtype)
+    batches = [(x, y)] + list(batches[1:])
+    print("bf16 C=768 long runs", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
+    for n in G:
+        assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+    row = slice(3 * 768, 4 * 768)  # wte is (Vp, C), row-major
+    assert rel_l2(G["wte"][row], O["wte"][row]) <= 2e-2

@@ -176,23 +176,28 @@ __device__ __forceinline__ void put_row(float* __restrict__ dst, const float acc
   d[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-// Lane l owns the 8-column chunks l, l+64, ... (NCH per lane) of a C-wide
-// row.  Rows are fetched EB_BATCH slots at a time so that that many loads
-// are in flight, then added in slot order.
+// A window's C columns are split over G waves (column groups of 64 chunks
+// of 8, so that twice as many waves run at C = 768); lane l of group g owns
+// chunk 64 g + l (NCH = 1) or chunks 64 (g NCH + k) + l.  Every group sees
+// the same runs and adds in the same slot order.  Rows are fetched EB_BATCH
+// slots at a time so that that many loads are in flight, then added in slot
+// order.
 constexpr int EB_BATCH = 8;
 
 template <class T, int NCH>
 __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ dx, int M, int C,
-                                                         const int32_t* __restrict__ sorted,
+                                                         int G, const int32_t* __restrict__ sorted,
                                                          const int32_t* __restrict__ stok,
                                                          float* __restrict__ dwte,
                                                          float* __restrict__ part) {
   const int lane = threadIdx.x % 64;
-  const int w = blockIdx.x * 4 + threadIdx.x / 64;
+  const int wg = blockIdx.x * 4 + threadIdx.x / 64;
+  const int w = wg / G, g = wg % G;
   const int s0 = w * EB_WIN;
   if (s0 >= M) return;
   const int n = min(EB_WIN, M - s0);
   const int nch = C / 8;
+  const int ch0 = 64 * NCH * g + lane;  // this lane's first chunk
   const int mytok = lane < n ? stok[s0 + lane] : -1;
   const int mypos = lane < n ? sorted[s0 + lane] : 0;
   const int prev_tok = s0 > 0 ? stok[s0 - 1] : -1;
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ d
       const T* row = dx + (int64_t)pos * C;
 #pragma unroll
       for (int k = 0; k < NCH; ++k) {
-        const int ch = lane + 64 * k;
+        const int ch = ch0 + 64 * k;
         if (i < n && ch < nch) load_row_chunk(row + ch * 8, rows[b][k]);
       }
     }
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ d
                             : part + ((int64_t)w * 2 + (from_prev ? 0 : 1)) * C;
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-          const int ch = lane + 64 * k;
+          const int ch = ch0 + 64 * k;
           if (ch < nch) {
             if (direct) add_row(dst + ch * 8, acc[k]);
             else put_row(dst + ch * 8, acc[k]);
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ d
 // next window: the token's segment (known from the scan) tells which windows
 // hold its partials.
 template <int NCH>
-__global__ __launch_bounds__(256) void emb_combine_kernel(int M, int C,
+__global__ __launch_bounds__(256) void emb_combine_kernel(int M, int C, int G,
                                                           const int32_t* __restrict__ stok,
                                                           const int32_t* __restrict__ total,
                                                           const int32_t* __restrict__ start,
@@ -260,7 +265,9 @@ __global__ __launch_bounds__(256) void emb_combine_kernel(int M, int C,
                                                           const float* __restrict__ part,
                                                           float* __restrict__ dwte) {
   const int lane = threadIdx.x % 64;
-  const int w = blockIdx.x * 4 + threadIdx.x / 64;
+  const int wg = blockIdx.x * 4 + threadIdx.x / 64;
+  const int w = wg / G, g = wg % G;
+  const int ch0 = 64 * NCH * g + lane;
   const int nwin = (int)cdiv(M, EB_WIN);
   if (w >= nwin) return;
   const int s0 = w * EB_WIN, n = min(EB_WIN, M - s0);
@@ -273,7 +280,7 @@ __global__ __launch_bounds__(256) void emb_combine_kernel(int M, int C,
   float acc[NCH][8];
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
-    const int ch = lane + 64 * k;
+    const int ch = ch0 + 64 * k;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[k][j] = 0.f;
     if (ch < nch) {
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(256) void emb_combine_kernel(int M, int C,
   for (int w2 = w + 1; w2 <= wend; ++w2) {
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const int ch = lane + 64 * k;
+      const int ch = ch0 + 64 * k;
       if (ch < nch) {
         const float* src = part + ((int64_t)w2 * 2) * C + ch * 8;
 #pragma unroll
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(256) void emb_combine_kernel(int M, int C,
   float* dst = dwte + (int64_t)t * C;
 #pragma unroll
   for (int k = 0; k < NCH; ++k) {
-    const int ch = lane + 64 * k;
+    const int ch = ch0 + 64 * k;
     if (ch < nch) add_row(dst + ch * 8, acc[k]);
   }
 }
@@ -325,23 +332,25 @@ hipError_t encoder_backward_wte(int dt, float* dwte, const void* dx, const int32
   emb_scan_kernel<<<1, 1024, 0, s>>>(sc.bsum, nsb);
   emb_place_kernel<<<(unsigned)cdiv(M, 256), 256, 0, s>>>(tok, M, V, sc.hist, sc.start, sc.bsum,
                                                           sc.lrank, sc.sorted, sc.stok);
-  const unsigned gw = (unsigned)cdiv(nwin, 4);
-  const int nchl = (int)cdiv(C / 8, 64);  // 8-column chunks per lane
+  // column groups: one chunk per lane up to C = 1024 (two groups at 768),
+  // two chunks per lane in at most two groups beyond
+  const int nchunks = C / 8;
+  const int nchl = nchunks <= 128 ? 1 : (int)cdiv(nchunks, 64 * 2);  // chunks per lane
+  const int G = (int)cdiv(nchunks, 64 * nchl);
+  const unsigned gw = (unsigned)cdiv((int64_t)nwin * G, 4);
 #define EMB_GO(NC)                                                                                \
   do {                                                                                            \
     if (dt == BF16)                                                                               \
-      emb_window_kernel<bf16, NC><<<gw, 256, 0, s>>>((const bf16*)dx, M, C, sc.sorted, sc.stok,   \
-                                                     dwte, sc.part);                              \
+      emb_window_kernel<bf16, NC><<<gw, 256, 0, s>>>((const bf16*)dx, M, C, G, sc.sorted,         \
+                                                     sc.stok, dwte, sc.part);                     \
     else                                                                                          \
-      emb_window_kernel<float, NC><<<gw, 256, 0, s>>>((const float*)dx, M, C, sc.sorted, sc.stok, \
-                                                      dwte, sc.part);                             \
-    emb_combine_kernel<NC><<<gw, 256, 0, s>>>(M, C, sc.stok, sc.total, sc.start, sc.bsum,        \
+      emb_window_kernel<float, NC><<<gw, 256, 0, s>>>((const float*)dx, M, C, G, sc.sorted,       \
+                                                      sc.stok, dwte, sc.part);                    \
+    emb_combine_kernel<NC><<<gw, 256, 0, s>>>(M, C, G, sc.stok, sc.total, sc.start, sc.bsum,     \
                                               sc.part, dwte);                                     \
   } while (0)
   if (nchl == 1) EMB_GO(1);
-  else if (nchl == 2) EMB_GO(2);
-  else if (nchl == 3) EMB_GO(3);
-  else EMB_GO(4);
+  else EMB_GO(2);
 #undef EMB_GO
   return hipGetLastError();
 }
