@@ -156,6 +156,71 @@ int gpt2_clip_and_adamw(gpt2_model* model, float lr, float beta1, float beta2, f
 /* Waits for the model's stream and reports pending device-side errors. */
 int gpt2_sync(gpt2_model* model);
 
+/* ---- Training-loop robustness.  The llm.c GPT-2 1.5B post (dszhyy.com)
+ * shows a training log with the z-score of the loss and of the gradient
+ * norm at every step (setup section), flags that save a checkpoint every n
+ * steps and resume a crashed run with bit-identical results (flags
+ * section), and a restart that skips an update whose loss or norm z-score
+ * exceeds 5 (results section).  These calls provide those pieces. */
+
+/* Rolling z-score detector over the last `window` finite values of a
+ * series, 2 <= window <= 65536 (host only, no GPU calls).
+ * gpt2_zscore_update sets *z_out to (x - mean) / std of the values held
+ * before x (population std, double precision), or NaN while fewer than
+ * `window` values are held, when x is not finite, or when std is 0; then it
+ * adds x if x is finite (the oldest value leaves).  z_out may be NULL. */
+typedef struct gpt2_zscore gpt2_zscore;
+int gpt2_zscore_create(int window, gpt2_zscore** out);
+int gpt2_zscore_update(gpt2_zscore* detector, double x, double* z_out);
+int gpt2_zscore_destroy(gpt2_zscore* detector);
+
+/* The optimizer step of gpt2_clip_and_adamw in two calls.  gpt2_grad_norm
+ * computes the global L2 norm of the gradients and the clip scale
+ * min(1, grad_clip / norm), waits, and returns the norm in *norm_out (host,
+ * may be NULL).  gpt2_adamw_update then applies clipping and AdamW with
+ * that norm exactly as gpt2_clip_and_adamw does (same result bit for bit).
+ * gpt2_adamw_update returns GPT2_ESTATE unless gpt2_grad_norm ran after the
+ * last change of the gradients (backward, zero_grad, set_grads,
+ * load_state), and GPT2_ENONFINITE (nothing updated, counted) when that
+ * norm was not finite.  gpt2_adamw_update does not wait. */
+int gpt2_grad_norm(gpt2_model* model, float grad_clip, float* norm_out);
+int gpt2_adamw_update(gpt2_model* model, float lr, float beta1, float beta2, float eps,
+                      float weight_decay);
+
+/* One guarded optimizer step: gpt2_grad_norm, the z-scores of `loss` in
+ * loss_z and of the norm in norm_z (gpt2_zscore_update: both values join
+ * their windows), then gpt2_adamw_update unless the norm is not finite
+ * (GPT2_ENONFINITE) or a z-score exceeds its threshold -- z_max_loss,
+ * z_max_norm; a detector that is NULL or a threshold <= 0 is not checked,
+ * a NaN z-score never triggers.  An outlier skip returns GPT2_OK with
+ * *skipped = 1; both kinds of skip leave parameters, m, v and the step
+ * count unchanged and are counted (gpt2_skip_counts).  norm_out, zloss_out,
+ * znorm_out and skipped may be NULL.  Waits for the stream. */
+int gpt2_guarded_step(gpt2_model* model, gpt2_zscore* loss_z, gpt2_zscore* norm_z, float loss,
+                      float z_max_loss, float z_max_norm, float lr, float beta1, float beta2,
+                      float eps, float weight_decay, float grad_clip, float* norm_out,
+                      double* zloss_out, double* znorm_out, int* skipped);
+
+/* Updates skipped since the model was created or loaded: for a non-finite
+ * gradient norm (here, in gpt2_clip_and_adamw and gpt2_adamw_update) and
+ * for a z-score outlier (gpt2_guarded_step).  Either pointer may be NULL. */
+int gpt2_skip_counts(gpt2_model* model, int64_t* nonfinite, int64_t* outlier);
+
+/* Checkpoints.  gpt2_save_state writes the fp32 parameters, AdamW m and v,
+ * the step count, the skip counts and the shape of the model to the file
+ * `path` (binary, native byte order: a 96-byte header, then params, m, v as
+ * num_params floats each).  gpt2_load_state reads such a file into a model
+ * of the same shape (n_layer, n_head, n_embd, block_size, vocab_size,
+ * padded_vocab_size; the dtype and batch shape may differ), refreshes the
+ * bf16 parameter copy and zeroes the gradients.  A run resumed from a
+ * checkpoint taken between optimizer steps, fed the same micro-batches,
+ * reproduces the uninterrupted run bit for bit: no other state carries
+ * from one step to the next.  EINVAL: the file cannot be opened, read or
+ * written, is short, has another magic or version, or another shape.  Both
+ * wait for the stream. */
+int gpt2_save_state(gpt2_model* model, const char* path);
+int gpt2_load_state(gpt2_model* model, const char* path);
+
 /* Debug / test reads of internal buffers (copied on the stream into dev_dst,
  * which must hold `bytes`).  which = GPT2_DBG_*; layer used by per-layer
  * buffers.  Element types: LOGITS, ACT_* in the activation dtype (fp32 or

@@ -14,7 +14,8 @@ import ctypes
 import os
 
 __all__ = [
-    "GPT2Config", "TensorInfo", "GPT2Error", "lib", "library_path", "Model", "param_layout",
+    "GPT2Config", "TensorInfo", "GPT2Error", "lib", "library_path", "Model", "ZScore",
+    "param_layout",
     "num_params", "workspace_bytes", "gemm", "gemm_colsum_ok", "gemm_workspace_bytes",
     "gemm_acc_group", "gemm_acc_group_workspace_bytes", "attention_forward", "attention_backward",
     "attention_colsum_ok",
@@ -67,8 +68,8 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{library_path} is missing: build it with "
                                "`python -m transformer_lm_pretraining_train_amd.build`")
         L = ctypes.CDLL(library_path)
-        P, I, I64, SZ, F = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
-                            ctypes.c_float)
+        P, I, I64, SZ, F, D = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                               ctypes.c_float, ctypes.c_double)
         CFG = ctypes.POINTER(GPT2Config)
         sig = {
             "gpt2_workspace_bytes": (SZ, [CFG]),
@@ -91,6 +92,16 @@ def lib() -> ctypes.CDLL:
             "gpt2_set_kernel_timer": (I, [P, I, I]),
             "gpt2_read_kernel_timer": (I, [P, ctypes.POINTER(I), ctypes.POINTER(ctypes.c_double)]),
             "gpt2_last_error": (ctypes.c_char_p, []),
+            "gpt2_zscore_create": (I, [I, ctypes.POINTER(P)]),
+            "gpt2_zscore_update": (I, [P, D, ctypes.POINTER(D)]),
+            "gpt2_zscore_destroy": (I, [P]),
+            "gpt2_grad_norm": (I, [P, F, ctypes.POINTER(F)]),
+            "gpt2_adamw_update": (I, [P, F, F, F, F, F]),
+            "gpt2_guarded_step": (I, [P, P, P, F, F, F, F, F, F, F, F, F, ctypes.POINTER(F),
+                                      ctypes.POINTER(D), ctypes.POINTER(D), ctypes.POINTER(I)]),
+            "gpt2_skip_counts": (I, [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+            "gpt2_save_state": (I, [P, ctypes.c_char_p]),
+            "gpt2_load_state": (I, [P, ctypes.c_char_p]),
             "gpt2k_gemm": (I, [I, I, I, I, I, I, P, I64, P, I64, I, P, I64, P, P, I64, P, I64, P,
                                I64, P, SZ, P]),
             "gpt2k_gemm_colsum_ok": (I, [I, I, I, I, I, I, I64, I64, I]),
@@ -255,6 +266,38 @@ class Model:
     def sync(self):
         _check(lib().gpt2_sync(self.h))
 
+    # ---- training-loop robustness (see gpt2.h)
+    def grad_norm(self, grad_clip=1.0):
+        n = ctypes.c_float()
+        _check(lib().gpt2_grad_norm(self.h, grad_clip, ctypes.byref(n)))
+        return n.value
+
+    def adamw_update(self, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1):
+        _check(lib().gpt2_adamw_update(self.h, lr, beta1, beta2, eps, weight_decay))
+
+    def guarded_step(self, loss, lr, loss_z=None, norm_z=None, z_max_loss=5.0, z_max_norm=5.0,
+                     beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, grad_clip=1.0):
+        """Returns dict(norm, z_loss, z_norm, skipped); a non-finite norm raises
+        GPT2Error (ENONFINITE) after counting the skip."""
+        n, zl, zn, sk = ctypes.c_float(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+        _check(lib().gpt2_guarded_step(
+            self.h, loss_z.h if loss_z is not None else None,
+            norm_z.h if norm_z is not None else None, float(loss), z_max_loss, z_max_norm, lr,
+            beta1, beta2, eps, weight_decay, grad_clip, ctypes.byref(n), ctypes.byref(zl),
+            ctypes.byref(zn), ctypes.byref(sk)))
+        return {"norm": n.value, "z_loss": zl.value, "z_norm": zn.value, "skipped": bool(sk.value)}
+
+    def skip_counts(self):
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().gpt2_skip_counts(self.h, ctypes.byref(a), ctypes.byref(b)))
+        return {"nonfinite": a.value, "outlier": b.value}
+
+    def save_state(self, path):
+        _check(lib().gpt2_save_state(self.h, os.fsencode(path)))
+
+    def load_state(self, path):
+        _check(lib().gpt2_load_state(self.h, os.fsencode(path)))
+
     def set_kernel_timer(self, name, max_launches=4096):
         """Bracket every launch of one step (TIMER key) with a HIP event pair."""
         _check(lib().gpt2_set_kernel_timer(self.h, TIMER[name], max_launches))
@@ -270,6 +313,29 @@ class Model:
         _check(lib().gpt2_debug_read(self.h, DBG[name], layer, _ptr(out),
                                      out.numel() * out.element_size()))
         return out
+
+
+class ZScore:
+    """Rolling z-score over the last ``window`` finite values (gpt2_zscore_*;
+    host only)."""
+
+    def __init__(self, window=128):
+        h = ctypes.c_void_p()
+        _check(lib().gpt2_zscore_create(window, ctypes.byref(h)))
+        self.h = h
+
+    def update(self, x):
+        z = ctypes.c_double()
+        _check(lib().gpt2_zscore_update(self.h, float(x), ctypes.byref(z)))
+        return z.value
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().gpt2_zscore_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()
 
 
 # ---- kernel-level entry points

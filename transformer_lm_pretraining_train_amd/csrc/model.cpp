@@ -180,6 +180,10 @@ struct gpt2_model {
   const int32_t* targets;
   bool have_targets;
   int64_t step;
+  // the norm of the current gradients (gpt2_grad_norm), valid until they change
+  bool norm_ready = false;
+  float norm_value = 0.f;
+  int64_t skips_nonfinite = 0, skips_outlier = 0;
   // optional HIP event pairs around one kind of launch (gpt2_set_kernel_timer)
   int timer_which = GPT2_TIMER_NONE;
   int timer_cap = 0, timer_used = 0;
@@ -492,6 +496,7 @@ int gpt2_get_grads(gpt2_model* md, float* dst) {
 
 int gpt2_set_grads(gpt2_model* md, const float* src) {
   if (!md || !src) return fail(GPT2_EINVAL, "NULL argument");
+  md->norm_ready = false;
   HIP_TRY(hipMemcpyAsync(md->grads, src, md->N * 4, hipMemcpyDeviceToDevice, md->stream));
   return GPT2_OK;
 }
@@ -514,6 +519,7 @@ int gpt2_set_opt_state(gpt2_model* md, const float* dm, const float* dv, int64_t
 
 int gpt2_zero_grad(gpt2_model* md) {
   if (!md) return fail(GPT2_EINVAL, "NULL model");
+  md->norm_ready = false;
   LAUNCH(fill_f32(md->grads, 0.f, md->N, md->stream));
   return GPT2_OK;
 }
@@ -584,6 +590,7 @@ int gpt2_backward(gpt2_model* md) {
   if (!md->have_targets)
     return fail(GPT2_ESTATE, "backward needs a preceding forward with targets");
   md->have_targets = false;
+  md->norm_ready = false;
   const int dt = md->dt;
   const int C = md->C, H = md->H, M = (int)md->M;
   const Layout& Ly = md->lay;
@@ -792,10 +799,195 @@ int gpt2_clip_and_adamw(gpt2_model* md, float lr, float beta1, float beta2, floa
   HIP_TRY(hipMemcpyAsync(res, grad_norm_result(md->norm_scratch), sizeof(res),
                          hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
-  if (!std::isfinite(res[0]))
+  md->norm_ready = false;
+  if (!std::isfinite(res[0])) {
+    ++md->skips_nonfinite;
     return fail(GPT2_ENONFINITE, "gradient norm is %f: update skipped", (double)res[0]);
+  }
   md->step = t;
   return gpt2_sync(md);
+}
+
+int gpt2_grad_norm(gpt2_model* md, float grad_clip, float* norm_out) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (!(grad_clip > 0.f)) return fail(GPT2_EINVAL, "grad_clip must be > 0");
+  hipStream_t s = md->stream;
+  LAUNCH(grad_norm(md->grads, md->N, grad_clip, md->norm_scratch, nullptr, s));
+  float res[2] = {0.f, 0.f};
+  HIP_TRY(hipMemcpyAsync(res, grad_norm_result(md->norm_scratch), sizeof(res),
+                         hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  md->norm_ready = true;
+  md->norm_value = res[0];
+  if (norm_out) *norm_out = res[0];
+  return GPT2_OK;
+}
+
+int gpt2_adamw_update(gpt2_model* md, float lr, float beta1, float beta2, float eps,
+                      float weight_decay) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (!md->norm_ready)
+    return fail(GPT2_ESTATE, "adamw_update needs gpt2_grad_norm after the last gradient change");
+  md->norm_ready = false;
+  if (!std::isfinite(md->norm_value)) {
+    ++md->skips_nonfinite;
+    return fail(GPT2_ENONFINITE, "gradient norm is %f: update skipped", (double)md->norm_value);
+  }
+  // the same launch as gpt2_clip_and_adamw, reading the norm and clip scale
+  // gpt2_grad_norm left in the norm scratch
+  const int64_t t = md->step + 1;
+  const float bc1 = (float)(1.0 - std::pow((double)beta1, (double)t));
+  const float bc2 = (float)(1.0 - std::pow((double)beta2, (double)t));
+  TIMED(GPT2_TIMER_ADAMW,
+        adamw(md->params, md->grads, md->m, md->v, md->dt == BF16 ? md->shadow : nullptr, md->N,
+              lr, beta1, beta2, eps, weight_decay, bc1, bc2, grad_norm_result(md->norm_scratch),
+              decay_map(md), md->stream));
+  md->step = t;
+  return GPT2_OK;
+}
+
+int gpt2_guarded_step(gpt2_model* md, gpt2_zscore* loss_z, gpt2_zscore* norm_z, float loss,
+                      float z_max_loss, float z_max_norm, float lr, float beta1, float beta2,
+                      float eps, float weight_decay, float grad_clip, float* norm_out,
+                      double* zloss_out, double* znorm_out, int* skipped) {
+  if (skipped) *skipped = 0;
+  float norm = 0.f;
+  int rc = gpt2_grad_norm(md, grad_clip, &norm);
+  if (rc != GPT2_OK) return rc;
+  if (norm_out) *norm_out = norm;
+  double zl = std::nan(""), zn = std::nan("");
+  if (loss_z && (rc = gpt2_zscore_update(loss_z, (double)loss, &zl)) != GPT2_OK) return rc;
+  if (norm_z && (rc = gpt2_zscore_update(norm_z, (double)norm, &zn)) != GPT2_OK) return rc;
+  if (zloss_out) *zloss_out = zl;
+  if (znorm_out) *znorm_out = zn;
+  if (!std::isfinite(norm)) {
+    md->norm_ready = false;
+    ++md->skips_nonfinite;
+    if (skipped) *skipped = 1;
+    return fail(GPT2_ENONFINITE, "gradient norm is %f: update skipped", (double)norm);
+  }
+  // a spike upwards is the instability; NaN z-scores (no history yet) never trigger
+  const bool outlier = (loss_z && z_max_loss > 0.f && zl > z_max_loss) ||
+                       (norm_z && z_max_norm > 0.f && zn > z_max_norm);
+  if (outlier) {
+    md->norm_ready = false;
+    ++md->skips_outlier;
+    if (skipped) *skipped = 1;
+    return GPT2_OK;
+  }
+  rc = gpt2_adamw_update(md, lr, beta1, beta2, eps, weight_decay);
+  if (rc != GPT2_OK) return rc;
+  return gpt2_sync(md);
+}
+
+int gpt2_skip_counts(gpt2_model* md, int64_t* nonfinite, int64_t* outlier) {
+  if (!md) return fail(GPT2_EINVAL, "NULL model");
+  if (nonfinite) *nonfinite = md->skips_nonfinite;
+  if (outlier) *outlier = md->skips_outlier;
+  return GPT2_OK;
+}
+
+namespace {
+
+// Checkpoint file: this header, then params, m, v (num_params floats each).
+struct CkptHeader {
+  char magic[8];
+  uint32_t version, header_bytes;
+  int32_t n_layer, n_head, n_embd, block_size, vocab_size, padded_vocab_size;
+  int32_t dtype, reserved0;
+  int64_t num_params, step, skips_nonfinite, skips_outlier;
+  int64_t reserved1[2];
+};
+static_assert(sizeof(CkptHeader) == 96, "checkpoint header layout");
+constexpr char kCkptMagic[8] = {'G', 'P', 'T', '2', 'C', 'K', 'P', 'T'};
+constexpr uint32_t kCkptVersion = 1;
+constexpr size_t kCkptChunk = size_t(64) << 20;  // bytes staged through host memory at a time
+
+struct File {
+  FILE* f = nullptr;
+  ~File() {
+    if (f) std::fclose(f);
+  }
+};
+
+}  // namespace
+
+int gpt2_save_state(gpt2_model* md, const char* path) {
+  if (!md || !path) return fail(GPT2_EINVAL, "NULL argument");
+  hipStream_t s = md->stream;
+  HIP_TRY(hipStreamSynchronize(s));
+  CkptHeader h{};
+  std::memcpy(h.magic, kCkptMagic, 8);
+  h.version = kCkptVersion;
+  h.header_bytes = sizeof(CkptHeader);
+  h.n_layer = md->cfg.n_layer;
+  h.n_head = md->cfg.n_head;
+  h.n_embd = md->cfg.n_embd;
+  h.block_size = md->cfg.block_size;
+  h.vocab_size = md->cfg.vocab_size;
+  h.padded_vocab_size = md->cfg.padded_vocab_size;
+  h.dtype = md->cfg.dtype;
+  h.num_params = md->N;
+  h.step = md->step;
+  h.skips_nonfinite = md->skips_nonfinite;
+  h.skips_outlier = md->skips_outlier;
+  File fh;
+  fh.f = std::fopen(path, "wb");
+  if (!fh.f) return fail(GPT2_EINVAL, "cannot open %s for writing", path);
+  if (std::fwrite(&h, sizeof(h), 1, fh.f) != 1) return fail(GPT2_EINVAL, "write to %s failed", path);
+  std::vector<char> buf(kCkptChunk);
+  for (const float* src : {md->params, md->m, md->v}) {
+    const size_t total = (size_t)md->N * sizeof(float);
+    for (size_t off = 0; off < total; off += kCkptChunk) {
+      const size_t n = std::min(kCkptChunk, total - off);
+      HIP_TRY(hipMemcpyAsync(buf.data(), (const char*)src + off, n, hipMemcpyDeviceToHost, s));
+      HIP_TRY(hipStreamSynchronize(s));
+      if (std::fwrite(buf.data(), 1, n, fh.f) != n) return fail(GPT2_EINVAL, "write to %s failed", path);
+    }
+  }
+  FILE* f = fh.f;
+  fh.f = nullptr;
+  if (std::fclose(f) != 0) return fail(GPT2_EINVAL, "closing %s failed", path);
+  return GPT2_OK;
+}
+
+int gpt2_load_state(gpt2_model* md, const char* path) {
+  if (!md || !path) return fail(GPT2_EINVAL, "NULL argument");
+  File fh;
+  fh.f = std::fopen(path, "rb");
+  if (!fh.f) return fail(GPT2_EINVAL, "cannot open %s", path);
+  CkptHeader h{};
+  if (std::fread(&h, sizeof(h), 1, fh.f) != 1) return fail(GPT2_EINVAL, "%s: short header", path);
+  if (std::memcmp(h.magic, kCkptMagic, 8) != 0 || h.version != kCkptVersion ||
+      h.header_bytes != sizeof(CkptHeader))
+    return fail(GPT2_EINVAL, "%s is not a version-%u checkpoint", path, kCkptVersion);
+  const gpt2_config& c = md->cfg;
+  if (h.n_layer != c.n_layer || h.n_head != c.n_head || h.n_embd != c.n_embd ||
+      h.block_size != c.block_size || h.vocab_size != c.vocab_size ||
+      h.padded_vocab_size != c.padded_vocab_size || h.num_params != md->N)
+    return fail(GPT2_EINVAL, "%s holds a model of another shape", path);
+  if (h.step < 0) return fail(GPT2_EINVAL, "%s: negative step count", path);
+  hipStream_t s = md->stream;
+  HIP_TRY(hipStreamSynchronize(s));
+  std::vector<char> buf(kCkptChunk);
+  for (float* dst : {md->params, md->m, md->v}) {
+    const size_t total = (size_t)md->N * sizeof(float);
+    for (size_t off = 0; off < total; off += kCkptChunk) {
+      const size_t n = std::min(kCkptChunk, total - off);
+      if (std::fread(buf.data(), 1, n, fh.f) != n) return fail(GPT2_EINVAL, "%s is short", path);
+      HIP_TRY(hipMemcpyAsync((char*)dst + off, buf.data(), n, hipMemcpyHostToDevice, s));
+      HIP_TRY(hipStreamSynchronize(s));
+    }
+  }
+  if (md->dt == BF16) LAUNCH(cast_f32_to_bf16(md->shadow, md->params, md->N, s));
+  LAUNCH(fill_f32(md->grads, 0.f, md->N, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  md->step = h.step;
+  md->skips_nonfinite = h.skips_nonfinite;
+  md->skips_outlier = h.skips_outlier;
+  md->norm_ready = false;
+  md->have_targets = false;
+  return GPT2_OK;
 }
 
 int gpt2_set_kernel_timer(gpt2_model* md, int which, int max_launches) {
