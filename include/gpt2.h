@@ -81,6 +81,12 @@ typedef struct {
                                 every reduction runs in a fixed order, so a step is bitwise
                                 repeatable for a given config and device */
   float ln_eps;              /* LayerNorm eps, 1e-5 */
+  int32_t recompute;         /* activations the backward regenerates instead of keeping one per
+                                layer (dszhyy.com llm.c 1.5B post, flags -r 1 / -r 2):
+                                0 none; 1 the GELU output (rewritten by the GELU-backward
+                                product from the kept pre-activation); 2 also the two
+                                LayerNorm outputs of each block (rerun from the kept block
+                                inputs).  Results are bit-identical across the three. */
 } gpt2_config;
 
 typedef struct {
@@ -229,7 +235,7 @@ enum {
   GPT2_DBG_LOGITS = 0,   /* (B*T, Vp) logits of the last forward, row pitch Vp */
   GPT2_DBG_LOSSES = 1,   /* (B*T) per-position cross-entropy */
   GPT2_DBG_ARGMAX = 2,   /* (B*T) argmax over the unpadded vocab, lowest index on ties */
-  GPT2_DBG_ACT_LN1 = 3,  /* (B*T, C) ln1 output of `layer` */
+  GPT2_DBG_ACT_LN1 = 3,  /* (B*T, C) ln1 output of `layer` (EINVAL with recompute = 2) */
   GPT2_DBG_ACT_QKV = 4,  /* (B*T, 3C) */
   GPT2_DBG_ACT_ATTY = 5, /* (B*T, C) attention output before the projection */
   GPT2_DBG_ACT_RES2 = 6, /* (B*T, C) residual after attention */

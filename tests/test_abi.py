@@ -67,6 +67,18 @@ def test_workspace_sizes_fit_288gb():
         assert 0 < nb < 200 * 2 ** 30, (name, nb)
 
 
+def test_recompute_shrinks_the_workspace():
+    """Recompute 1 drops the per-layer GELU outputs (L x B*T*4C) for four
+    shared buffers, recompute 2 also the per-layer LayerNorm outputs (2L x
+    B*T*C) for seven (the flags -r 1 / -r 2 of the llm.c 1.5B post)."""
+    wl = synth.workload("gpt2_124m")
+    cfg = [g.config_for(wl, recompute=r) for r in range(3)]
+    nb = [g.workspace_bytes(c) for c in cfg]
+    M, C, L, es = wl.micro_batch * wl.seq_len, wl.n_embd, wl.n_layer, 2
+    assert nb[0] - nb[1] == pytest.approx((L - 4) * M * 4 * C * es, rel=1e-4)
+    assert nb[1] - nb[2] == pytest.approx((2 * L - 7) * M * C * es, rel=1e-4)
+
+
 def test_deterministic_flag_accepted():
     cfg = g.config_for(synth.workload("tiny"))
     cfg.deterministic = 1
@@ -75,7 +87,7 @@ def test_deterministic_flag_accepted():
 
 @pytest.mark.parametrize("field,value", [
     ("n_embd", 100), ("n_head", 7), ("seq_len", 2048), ("padded_vocab_size", 10),
-    ("dtype", 5), ("micro_batch", 0), ("ln_eps", 0.0)])
+    ("dtype", 5), ("micro_batch", 0), ("ln_eps", 0.0), ("recompute", 3), ("recompute", -1)])
 def test_invalid_configs_rejected(field, value):
     cfg = g.config_for(synth.workload("tiny"))
     setattr(cfg, field, value)

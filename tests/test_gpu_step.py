@@ -383,3 +383,24 @@ def test_bf16_width_768_long_token_runs_match_oracle():
         assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
     row = slice(3 * 768, 4 * 768)  # wte is (Vp, C), row-major
     assert rel_l2(G["wte"][row], O["wte"][row]) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype,shape", [("fp32", {}), ("bf16", dict(B=4, n_layer=2, n_embd=768,
+                                                                     n_head=12))])
+def test_recompute_is_bit_identical(dtype, shape):
+    """Recomputing the GELU output (recompute 1) and also the LayerNorm
+    outputs (recompute 2) in the backward gives the same losses, gradients
+    and updated parameters bit for bit as keeping them: two optimizer steps
+    of two micro-steps."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", dtype, k=2, **shape)
+    print(f"{dtype} recompute 0/1/2", flush=True)
+    res = []
+    for r in range(3):
+        cfg.recompute = r
+        _, gs = gpu_step(cfg, flat, batches, steps=2)
+        res.append(gs)
+    for r in (1, 2):
+        for s0, s1 in zip(res[0], res[r]):
+            assert s0["losses"] == s1["losses"]
+            assert np.array_equal(s0["grads"], s1["grads"])
+            assert np.array_equal(s0["params"], s1["params"])

@@ -49,6 +49,8 @@ __device__ __forceinline__ float epi_apply(const Epilogue& e, int m, int n, floa
   } else if constexpr (MODE == EPI_GELU_BWD) {
     float h = to_f(((const T*)e.aux)[(int64_t)m * e.ldx + n]);
     y = from_f<T>(acc * gelu_grad_f(h));
+    // out2 (optional): GELU(h) again, as the forward's bias + GELU epilogue stored it
+    if (e.out2) ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(h));
   } else {  // EPI_ACC_F32
     float* of = (float*)e.out + (int64_t)m * e.ldo + n;
     *of += acc;
@@ -312,6 +314,12 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
         Pack<bf16> h = load_pack((const bf16*)e.aux + (int64_t)m * e.ldx + n);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] *= gelu_grad_f(to_f(h.e[j]));
+        if (e.out2) {  // GELU(h) again, as the forward's bias + GELU epilogue stored it
+          Pack<bf16> g2;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) g2.e[j] = (bf16)gelu_f(to_f(h.e[j]));
+          store_pack((bf16*)e.out2 + (int64_t)m * e.ldo2 + n, g2);
+        }
       }
       Pack<bf16> o;
 #pragma unroll

@@ -121,6 +121,7 @@ int validate(const gpt2_config* c) {
     return fail(GPT2_EINVAL, "micro_batch * seq_len too large");
   if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16) return fail(GPT2_EINVAL, "dtype must be 0 or 1");
   if (!(c->ln_eps > 0.f)) return fail(GPT2_EINVAL, "ln_eps must be > 0");
+  if (c->recompute < 0 || c->recompute > 2) return fail(GPT2_EINVAL, "recompute must be 0, 1 or 2");
   return GPT2_OK;
 }
 
@@ -160,6 +161,14 @@ struct gpt2_model {
   // the first layer (the embedding gradient); dbuf_c: scratch activation
   // gradient.
   void *bw_in[3], *bw_mid[3], *bw_d4[3], *bw_dq[3];
+  // recompute >= 1: the forward's GELU output goes to fchg_tmp (read at once
+  // by the next product) and the backward regenerates each layer's into
+  // bw_fchg[set]; recompute 2: the same for the LayerNorm outputs (ln_tmp,
+  // bw_ln1 / bw_ln2).  Null otherwise.
+  void* fchg_tmp = nullptr;
+  void* ln_tmp = nullptr;
+  void *bw_fchg[3] = {nullptr, nullptr, nullptr};
+  void *bw_ln1[3] = {nullptr, nullptr, nullptr}, *bw_ln2[3] = {nullptr, nullptr, nullptr};
   // A second stream for the weight-gradient launches of two layers, which
   // fill 216 of the 256 CUs: the next layer's work runs beside them.
   hipStream_t side = nullptr;
@@ -228,19 +237,30 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.act.resize(c.n_layer);
   for (int l = 0; l < c.n_layer; ++l) {
     LayerAct& a = md.act[l];
-    a.ln1 = cv.take(M * C * es);
+    a.ln1 = c.recompute >= 2 ? nullptr : cv.take(M * C * es);
     a.ln1_mean = (float*)cv.take(M * 4);
     a.ln1_rstd = (float*)cv.take(M * 4);
     a.qkv = cv.take(M * 3 * C * es);
     a.atty = cv.take(M * C * es);
     a.lse = (float*)cv.take((int64_t)c.micro_batch * H * c.seq_len * 4);
     a.res2 = cv.take(M * C * es);
-    a.ln2 = cv.take(M * C * es);
+    a.ln2 = c.recompute >= 2 ? nullptr : cv.take(M * C * es);
     a.ln2_mean = (float*)cv.take(M * 4);
     a.ln2_rstd = (float*)cv.take(M * 4);
     a.fch = cv.take(M * 4 * C * es);
-    a.fchg = cv.take(M * 4 * C * es);
+    a.fchg = c.recompute >= 1 ? nullptr : cv.take(M * 4 * C * es);
     a.res3 = cv.take(M * C * es);
+  }
+  if (c.recompute >= 1) {
+    md.fchg_tmp = cv.take(M * 4 * C * es);
+    for (int i = 0; i < 3; ++i) md.bw_fchg[i] = cv.take(M * 4 * C * es);
+  }
+  if (c.recompute >= 2) {
+    md.ln_tmp = cv.take(M * C * es);
+    for (int i = 0; i < 3; ++i) {
+      md.bw_ln1[i] = cv.take(M * C * es);
+      md.bw_ln2[i] = cv.take(M * C * es);
+    }
   }
   md.lnf = cv.take(M * C * es);
   md.lnf_mean = (float*)cv.take(M * 4);
@@ -542,11 +562,14 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   for (int l = 0; l < md->L; ++l) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
-    LAUNCH(layernorm_forward(dt, a.ln1, a.ln1_mean, a.ln1_rstd, x, P + o.ln1_w, P + o.ln1_b, M, C,
+    void* ln1 = a.ln1 ? a.ln1 : md->ln_tmp;  // recompute 2: not kept
+    void* ln2 = a.ln2 ? a.ln2 : md->ln_tmp;
+    void* fchg = a.fchg ? a.fchg : md->fchg_tmp;  // recompute >= 1: not kept
+    LAUNCH(layernorm_forward(dt, ln1, a.ln1_mean, a.ln1_rstd, x, P + o.ln1_w, P + o.ln1_b, M, C,
                              eps, s));
     Epilogue e = epi(EPI_BIAS, a.qkv, 3 * C);
     e.bias = P + o.qkv_b;
-    LAUNCH(gemm(dt, true, true, M, 3 * C, C, a.ln1, C, md->wt(o.qkv_w), C, e, s));
+    LAUNCH(gemm(dt, true, true, M, 3 * C, C, ln1, C, md->wt(o.qkv_w), C, e, s));
     TIMED(GPT2_TIMER_ATTN_FWD,
           attention_forward(dt, a.atty, a.lse, a.qkv, md->B, md->Tn, H, md->hd, s));
     e = epi(EPI_BIAS_RESID, a.res2, C);
@@ -554,18 +577,18 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     e.resid = x;
     e.ldr = C;
     LAUNCH(gemm(dt, true, true, M, C, C, a.atty, C, md->wt(o.proj_w), C, e, s));
-    LAUNCH(layernorm_forward(dt, a.ln2, a.ln2_mean, a.ln2_rstd, a.res2, P + o.ln2_w, P + o.ln2_b, M,
+    LAUNCH(layernorm_forward(dt, ln2, a.ln2_mean, a.ln2_rstd, a.res2, P + o.ln2_w, P + o.ln2_b, M,
                              C, eps, s));
     e = epi(EPI_BIAS_GELU, a.fch, 4 * C);
     e.bias = P + o.fc_b;
-    e.out2 = a.fchg;
+    e.out2 = fchg;
     e.ldo2 = 4 * C;
-    LAUNCH(gemm(dt, true, true, M, 4 * C, C, a.ln2, C, md->wt(o.fc_w), C, e, s));
+    LAUNCH(gemm(dt, true, true, M, 4 * C, C, ln2, C, md->wt(o.fc_w), C, e, s));
     e = epi(EPI_BIAS_RESID, a.res3, C);
     e.bias = P + o.fcp_b;
     e.resid = a.res2;
     e.ldr = C;
-    LAUNCH(gemm(dt, true, true, M, C, 4 * C, a.fchg, 4 * C, md->wt(o.fcp_w), 4 * C, e, s));
+    LAUNCH(gemm(dt, true, true, M, C, 4 * C, fchg, 4 * C, md->wt(o.fcp_w), 4 * C, e, s));
     x = a.res3;
   }
   LAUNCH(layernorm_forward(dt, md->lnf, md->lnf_mean, md->lnf_rstd, x, P + Ly.lnf_w, P + Ly.lnf_b,
@@ -662,9 +685,24 @@ int gpt2_backward(gpt2_model* md) {
     void* dq = md->bw_dq[set];
     LAUNCH(guard(set));
     // MLP output projection: res3 = res2 + fchg fcp_w^T + fcp_b
+    // recomputed activations of this layer (bit-identical to the forward's:
+    // the same kernels on the same kept inputs)
+    void* fchg = a.fchg ? a.fchg : md->bw_fchg[set];
+    void* ln2 = a.ln2 ? a.ln2 : md->bw_ln2[set];
+    void* ln1 = a.ln1 ? a.ln1 : md->bw_ln1[set];
+    if (!a.ln2)
+      LAUNCH(layernorm_forward(dt, ln2, a.ln2_mean, a.ln2_rstd, a.res2, P + o.ln2_w, P + o.ln2_b,
+                               M, C, md->cfg.ln_eps, s));
+    if (!a.ln1)
+      LAUNCH(layernorm_forward(dt, ln1, a.ln1_mean, a.ln1_rstd, xin, P + o.ln1_w, P + o.ln1_b, M,
+                               C, md->cfg.ln_eps, s));
     Epilogue e = epi(EPI_GELU_BWD, d4, 4 * C);
     e.aux = a.fch;
     e.ldx = 4 * C;
+    if (!a.fchg) {  // the GELU output again, from the pre-activation this product reads
+      e.out2 = fchg;
+      e.ldo2 = 4 * C;
+    }
     // d fc_b = column sums of d4: per 64-row block in the product's epilogue
     // where it can, else a pass over d4 after the next product
     const bool fcb_fused = gemm_colsum_ok(dt, true, false, M, 4 * C, C, C, 4 * C, EPI_GELU_BWD);
@@ -713,10 +751,10 @@ int gpt2_backward(gpt2_model* md) {
     }
     // the layer's weight gradients dW += dy^T x
     const AccItem dw[4] = {
-        {C, 4 * C, in, C, a.fchg, 4 * C, G + o.fcp_w, 4 * C},
-        {4 * C, C, d4, 4 * C, a.ln2, C, G + o.fc_w, C},
+        {C, 4 * C, in, C, fchg, 4 * C, G + o.fcp_w, 4 * C},
+        {4 * C, C, d4, 4 * C, ln2, C, G + o.fc_w, C},
         {C, C, mid, C, a.atty, C, G + o.proj_w, C},
-        {3 * C, C, dq, 3 * C, a.ln1, C, G + o.qkv_w, C}};
+        {3 * C, C, dq, 3 * C, ln1, C, G + o.qkv_w, C}};
     std::copy(dw, dw + 4, pend + npend);
     npend += 4;
     if (npend == 8) {
@@ -1050,7 +1088,11 @@ int gpt2_debug_read(gpt2_model* md, int which, int layer, void* dst, size_t byte
     case GPT2_DBG_ATT_LSE: {
       if (!need_layer()) return fail(GPT2_EINVAL, "layer %d out of range", layer);
       const LayerAct& a = md->act[layer];
-      if (which == GPT2_DBG_ACT_LN1) { src = a.ln1; n = M * C * es; }
+      if (which == GPT2_DBG_ACT_LN1) {
+        if (!a.ln1) return fail(GPT2_EINVAL, "ln1 outputs are not kept with recompute = 2");
+        src = a.ln1;
+        n = M * C * es;
+      }
       if (which == GPT2_DBG_ACT_QKV) { src = a.qkv; n = M * 3 * C * es; }
       if (which == GPT2_DBG_ACT_ATTY) { src = a.atty; n = M * C * es; }
       if (which == GPT2_DBG_ACT_RES2) { src = a.res2; n = M * C * es; }
