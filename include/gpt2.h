@@ -140,6 +140,20 @@ int gpt2_set_opt_state(gpt2_model* model, const float* dev_m, const float* dev_v
 int gpt2_forward(gpt2_model* model, const int32_t* dev_tokens, const int32_t* dev_targets,
                  float* dev_loss);
 
+/* Evaluation forward: the loss of gpt2_forward with targets (dev_targets
+ * required; mean written to dev_loss, may be NULL; per-position losses
+ * readable as GPT2_DBG_LOSSES) without materialising the B*T x Vp logits:
+ * in bf16 the tied head's product leaves only each row's (max, sum of
+ * exponentials) per 128 vocabulary columns and the target's logit, which
+ * one more pass combines into log-sum-exp and loss (the extension of the
+ * fused classifier that never stores the logits; dszhyy.com llm.c 1.5B
+ * post, PyTorch-comparison section).  In fp32, or for shapes the large
+ * tiles do not cover, the logits are computed and the loss taken from them.
+ * Neither the logits nor their gradient are left for reading, and a
+ * following gpt2_backward returns GPT2_ESTATE.  Ids as in gpt2_forward. */
+int gpt2_forward_loss(gpt2_model* model, const int32_t* dev_tokens, const int32_t* dev_targets,
+                      float* dev_loss);
+
 /* Backward pass of the last forward (which must have had targets):
  * gradients += d(mean loss / k) / d params.  The logit gradient comes from
  * the forward's cross-entropy (computed with the loss, from the same read of

@@ -404,3 +404,39 @@ def test_recompute_is_bit_identical(dtype, shape):
             assert s0["losses"] == s1["losses"]
             assert np.array_equal(s0["grads"], s1["grads"])
             assert np.array_equal(s0["params"], s1["params"])
+
+
+@pytest.mark.parametrize("dtype,shape", [
+    ("fp32", {}),  # the logits, then the loss
+    ("bf16", dict(B=2, n_layer=1)),  # 128 rows: the logits, then the loss
+    ("bf16", dict(B=4, n_layer=1, padded_vocab_size=300)),  # row statistics, a ragged tile
+    ("bf16", dict(B=4, n_layer=1, vocab_size=50257, padded_vocab_size=50304)),
+])
+def test_forward_loss_without_logits_matches_forward(dtype, shape):
+    """The evaluation forward (row statistics of the tied head, no logits)
+    gives the per-position losses of the training forward, which reads the
+    stored logits: same bf16 logit values, sums in another order.  With
+    the GPT-2 vocabulary the padded columns stay out of the sums."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", dtype, **shape)
+    print(f"{dtype} forward_loss {shape}", flush=True)
+    m = g.Model(cfg)
+    m.set_params(to_dev(flat))
+    x, y = batches[0]
+    xt, yt = to_dev(x), to_dev(y)
+    M = x.size
+    la, lb = torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda")
+    pa, pb = torch.zeros(M, device="cuda"), torch.zeros(M, device="cuda")
+    m.forward(xt, yt, la)
+    m.debug_read("losses", pa)
+    m.forward_loss(xt, yt, lb)
+    m.debug_read("losses", pb)
+    torch.cuda.synchronize()
+    ra, rb = host(pa), host(pb)
+    np.testing.assert_allclose(rb, ra, rtol=2e-6, atol=2e-6)
+    assert float(lb) == pytest.approx(float(la), rel=2e-6)
+    with pytest.raises(g.GPT2Error) as ei:  # nothing to differentiate
+        m.backward()
+    assert ei.value.name == "ESTATE"
+    orr = oracle_steps(ocfg, flat, [batches[0]])[0]
+    tol = 1e-4 if dtype == "fp32" else 1e-2
+    assert abs(float(lb) - orr["losses"][0]) <= tol * orr["losses"][0]

@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "gpt2_set_kernel_timer": (I, [P, I, I]),
             "gpt2_read_kernel_timer": (I, [P, ctypes.POINTER(I), ctypes.POINTER(ctypes.c_double)]),
             "gpt2_last_error": (ctypes.c_char_p, []),
+            "gpt2_forward_loss": (I, [P, P, P, P]),
             "gpt2_zscore_create": (I, [I, ctypes.POINTER(P)]),
             "gpt2_zscore_update": (I, [P, D, ctypes.POINTER(D)]),
             "gpt2_zscore_destroy": (I, [P]),
@@ -249,6 +250,11 @@ class Model:
     # ---- the step
     def forward(self, tokens, targets=None, loss_out=None):
         _check(lib().gpt2_forward(self.h, _ptr(tokens), _ptr(targets), _ptr(loss_out)))
+        return loss_out
+
+    def forward_loss(self, tokens, targets, loss_out=None):
+        """The loss alone, without materialising the logits (gpt2_forward_loss)."""
+        _check(lib().gpt2_forward_loss(self.h, _ptr(tokens), _ptr(targets), _ptr(loss_out)))
         return loss_out
 
     def backward(self):

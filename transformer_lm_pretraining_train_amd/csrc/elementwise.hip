@@ -760,6 +760,49 @@ __global__ __launch_bounds__(256) void mean_loss_kernel(float* __restrict__ out,
   if (threadIdx.x == 0) out[0] = (float)((part[0] + part[1] + part[2] + part[3]) / M);
 }
 
+// One wave per row: the row's gemm_rowstats groups combined lane-strided,
+// then by a shuffle tree (fixed order), into lse and the loss.
+__global__ __launch_bounds__(256) void rowstats_loss_kernel(float* __restrict__ losses,
+                                                            float* __restrict__ lse_out,
+                                                            const float2* __restrict__ stats,
+                                                            int64_t ld, int ncols,
+                                                            const float* __restrict__ tgt,
+                                                            const int32_t* __restrict__ targets,
+                                                            int M, int V, int* __restrict__ flag) {
+  const int lane = threadIdx.x % 64;
+  const int row = blockIdx.x * 4 + threadIdx.x / 64;
+  if (row >= M) return;  // wave-uniform
+  auto combine = [](float& m1, float& s1, float m2, float s2) {
+    const float m = fmaxf(m1, m2);
+    if (m == -INFINITY) return;
+    s1 = s1 * fast_exp(m1 - m) + s2 * fast_exp(m2 - m);
+    m1 = m;
+  };
+  float m = -INFINITY, sum = 0.f;
+  for (int h = lane; h < ncols; h += 64) {
+    const float2 st = stats[(int64_t)row * ld + h];
+    combine(m, sum, st.x, st.y);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) combine(m, sum, __shfl_xor(m, o, 64), __shfl_xor(sum, o, 64));
+  if (lane == 0) {
+    const float lse = m + logf(sum);
+    const int y = targets[row];
+    if (y < 0 || y >= V) atomicOr(flag, 2);
+    losses[row] = lse - tgt[row];
+    lse_out[row] = lse;
+  }
+}
+
+hipError_t rowstats_loss(float* losses, float* lse, const float2* stats, int64_t ld, int ncols,
+                         const float* tgt, const int32_t* targets, int M, int V, int* err_flag,
+                         hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  rowstats_loss_kernel<<<(unsigned)cdiv(M, 4), 256, 0, s>>>(losses, lse, stats, ld, ncols, tgt,
+                                                             targets, M, V, err_flag);
+  return hipGetLastError();
+}
+
 hipError_t mean_loss(float* out, const float* losses, int M, hipStream_t s) {
   mean_loss_kernel<<<1, 256, 0, s>>>(out, losses, M);
   return hipGetLastError();

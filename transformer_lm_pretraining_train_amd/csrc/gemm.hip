@@ -653,6 +653,19 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
   // into the slab, and lane c < 16 JB sums slab columns 2c, 2c+1 over the
   // 32 rows, then over the wave's TI row blocks -- the wave's WM = 64 rows,
   // one colsum block.
+  // Softmax row statistics (EPI_ROWSTATS): lane l of a 256-column tile
+  // handles rows l/8 + 8t (t < 4) of the slab and columns 8 (l%8) .. +8; the
+  // eight lanes of a row combine their (max, sum) by shuffles, and across
+  // the wave's two column rounds, into one entry per row and 128 columns.
+  constexpr bool kStats = MODE == EPI_ROWSTATS;
+  static_assert(!kStats || (BN == 256 && JB == 2), "row statistics need 256-column tiles");
+  float rmax[kStats ? 4 : 1], rsum[kStats ? 4 : 1];
+  auto combine = [](float& m1, float& s1, float m2, float s2) {
+    const float m = fmaxf(m1, m2);
+    if (m == -INFINITY) return;  // both empty
+    s1 = s1 * fast_exp(m1 - m) + s2 * fast_exp(m2 - m);
+    m1 = m;
+  };
   constexpr bool kColsum = MODE == EPI_GELU_BWD;
   static_assert(!kColsum || WM == 64, "colsum blocks are the waves' 64 rows");
   const bool colsum = kColsum && e.colsum != nullptr;
@@ -662,6 +675,13 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
+    if constexpr (kStats) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        rmax[t] = -INFINITY;
+        rsum[t] = 0.f;
+      }
+    }
 #pragma unroll
     for (int jr = 0; jr < TJ / JB; ++jr) {
 #pragma unroll
@@ -684,6 +704,30 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         const float4 b = *reinterpret_cast<const float4*>(slab + row * SP + col + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const int m = m0 + wm * WM + i * 32 + row, n = n0 + wn * WN + jr * JB * 32 + col;
+        if constexpr (kStats) {
+          // e.ldx = V (valid columns), e.aux = targets, e.out2 = tgt
+          const int V = (int)e.ldx;
+          float z[8], cm = -INFINITY, cs = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            z[j] = (float)(bf16)v[j];
+            if (m < M && n + j < V) cm = fmaxf(cm, z[j]);
+          }
+          if (cm != -INFINITY) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (m < M && n + j < V) cs += fast_exp(z[j] - cm);
+          }
+          if (m < M) {
+            const int y = min(max(((const int32_t*)e.aux)[m], 0), V - 1);
+            if (y >= n && y < n + 8) ((float*)e.out2)[m] = z[y - n];
+          }
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1)
+            combine(cm, cs, __shfl_xor(cm, o, 64), __shfl_xor(cs, o, 64));
+          combine(rmax[t], rsum[t], cm, cs);
+          continue;
+        }
         float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, split, M, res);
         if (colsum) {  // this lane alone read these slab entries
@@ -704,6 +748,16 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         csum[jr].y += t.y;
       }
       __builtin_amdgcn_wave_barrier();
+    }
+    if constexpr (kStats) {
+      if (lane % 8 == 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int m = m0 + wm * WM + i * 32 + lane / 8 + 8 * t;
+          if (m < M)
+            ((float2*)e.out)[(int64_t)m * e.ldo + n0 / 128 + wn] = make_float2(rmax[t], rsum[t]);
+        }
+      }
     }
   }
   if (colsum && lane < 16 * JB) {
@@ -1037,6 +1091,38 @@ bool gemm_colsum_ok(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, i
   const Plan p = plan_gemm(M, N, K, mode);
   return p.kind != 0 && operand_span(a_kmajor, M, K, lda) < (int64_t(1) << 31) &&
          operand_span(b_kmajor, N, K, ldb) < (int64_t(1) << 31);
+}
+
+bool gemm_rowstats_ok(int dt, int M, int N, int K, int64_t lda, int64_t ldb) {
+  return dt == BF16 && M >= 256 && N >= 256 && K > 0 && K % 8 == 0 && lda % 8 == 0 &&
+         ldb % 8 == 0 && lda >= K && ldb >= K && operand_span(true, M, K, lda) < (int64_t(1) << 31) &&
+         operand_span(true, N, K, ldb) < (int64_t(1) << 31);
+}
+
+hipError_t gemm_rowstats(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, int V, const int32_t* target, float2* stats, int64_t ld,
+                         float* tgt, hipStream_t s) {
+  if (!gemm_rowstats_ok(BF16, M, N, K, lda, ldb)) return hipErrorNotSupported;
+  if (V < 1 || V > N || ld < gemm_rowstats_cols(N) || !target || !stats || !tgt)
+    return hipErrorInvalidValue;
+  Epilogue e{};
+  e.mode = EPI_ROWSTATS;
+  e.out = stats;
+  e.ldo = ld;
+  e.aux = target;
+  e.ldx = V;
+  e.out2 = tgt;
+  const int tiles_m = (int)cdiv(M, 256), tiles_n = (int)cdiv(N, 256);
+  const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+  BigBatch batch{};
+  batch.p[0] = BigProblem{M, N, tiles_m, tiles_n, (const bf16*)A, lda, (const bf16*)B, ldb, e};
+  batch.grouped = 0;
+  batch.n = 1;
+  batch.splits = 1;
+  dim3 grid((unsigned)(ntiles < kCUs ? ntiles : kCUs), 1);
+  gemm_big_kernel<256, 256, true, true, EPI_ROWSTATS><<<grid, BIG_THREADS, 0, s>>>(
+      batch, K, (int)round_up(K, 64));
+  return hipGetLastError();
 }
 
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,

@@ -96,7 +96,8 @@ enum EpiMode {
   EPI_BIAS_GELU = 3,   // out = acc + bias[n]; out2 = gelu(out)
   EPI_GELU_BWD = 4,    // out = acc * gelu'(aux[m, n]); out2 (if not null) = gelu(aux[m, n])
   EPI_ACC_F32 = 5,     // out (fp32) += acc
-  EPI_PARTIAL = 6      // internal: split-K partial tile, fp32
+  EPI_PARTIAL = 6,     // internal: split-K partial tile, fp32
+  EPI_ROWSTATS = 7     // internal: softmax row statistics, see gemm_rowstats()
 };
 struct Epilogue {
   int mode;
@@ -129,6 +130,25 @@ hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const
 bool gemm_colsum_ok(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, int64_t lda,
                     int64_t ldb, int mode);
 inline int gemm_colsum_blocks(int M) { return (M + 63) / 64; }
+// Softmax statistics of the rows of z = bf16(A B^T) (A, B k-major) without
+// storing z -- the loss of the tied head without its logits: for each row m
+// and each 128-column group h (columns [128 h, 128 h + 128) ∩ [0, V)),
+// stats[m * ld + h] = (max z, sum exp(z - max)) over those columns ((-inf, 0)
+// if none), and tgt[m] = z[m, y] with y = target[m] clamped to [0, V).  Only
+// bf16 products on the 256 x 256 tiles (gemm_rowstats_ok); ld >=
+// gemm_rowstats_cols(N).
+bool gemm_rowstats_ok(int dt, int M, int N, int K, int64_t lda, int64_t ldb);
+inline int gemm_rowstats_cols(int N) { return 2 * ((N + 255) / 256); }
+hipError_t gemm_rowstats(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, int V, const int32_t* target, float2* stats, int64_t ld,
+                         float* tgt, hipStream_t s);
+// loss[m] = log sum_h stats[m, h].s exp(stats[m, h].max - M) + M - tgt[m]
+// (M the largest max), combining each row's gemm_rowstats groups in a
+// fixed order; lse[m] also written; out-of-range targets set bit 2 of
+// err_flag.
+hipError_t rowstats_loss(float* losses, float* lse, const float2* stats, int64_t ld, int ncols,
+                         const float* tgt, const int32_t* targets, int M, int V, int* err_flag,
+                         hipStream_t s);
 // out (fp32, pitch ldo) += sum_k A[k * lda + m] B[k * ldb + n] for m < M,
 // n < N: a weight gradient dW += dy^T x with dy and x stored row-major.
 struct AccItem {

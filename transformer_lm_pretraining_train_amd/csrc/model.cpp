@@ -544,7 +544,8 @@ int gpt2_zero_grad(gpt2_model* md) {
   return GPT2_OK;
 }
 
-int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, float* dev_loss) {
+// Embeddings, the blocks and the final LayerNorm (into md->lnf).
+static int forward_trunk(gpt2_model* md, const int32_t* tokens, const int32_t* targets) {
   if (!md || !tokens) return fail(GPT2_EINVAL, "NULL argument");
   const int dt = md->dt;
   const int C = md->C, H = md->H, M = (int)md->M;
@@ -593,6 +594,16 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
   }
   LAUNCH(layernorm_forward(dt, md->lnf, md->lnf_mean, md->lnf_rstd, x, P + Ly.lnf_w, P + Ly.lnf_b,
                            M, C, eps, s));
+  return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, float* dev_loss) {
+  const int rc = forward_trunk(md, tokens, targets);
+  if (rc != GPT2_OK) return rc;
+  const int dt = md->dt;
+  const int C = md->C, M = (int)md->M;
+  const Layout& Ly = md->lay;
+  hipStream_t s = md->stream;
   // logits over the padded vocabulary (tied head: wte)
   TIMED(GPT2_TIMER_LM_HEAD_FWD, gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
                                      epi(EPI_STORE, md->logits, md->ldl), s));
@@ -605,6 +616,36 @@ int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, 
     LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
     md->have_targets = true;
   }
+  return GPT2_OK;
+}
+
+int gpt2_forward_loss(gpt2_model* md, const int32_t* tokens, const int32_t* targets,
+                      float* dev_loss) {
+  if (!md || !tokens || !targets) return fail(GPT2_EINVAL, "NULL argument");
+  const int rc = forward_trunk(md, tokens, targets);
+  if (rc != GPT2_OK) return rc;
+  const int dt = md->dt, C = md->C, M = (int)md->M;
+  const Layout& Ly = md->lay;
+  hipStream_t s = md->stream;
+  if (gemm_rowstats_ok(dt, M, md->Vp, C, C, C)) {
+    // per-row (max, sum) of every 128 logits and the target's logit, never
+    // the logits themselves; the gradient buffer (unused without a
+    // backward) holds them
+    const int ncols = gemm_rowstats_cols(md->Vp);
+    float2* stats = (float2*)md->dlogits;
+    float* tgt = (float*)((char*)md->dlogits + round_up((int64_t)M * ncols * 8, 256));
+    LAUNCH(gemm_rowstats(M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C, md->V, targets, stats,
+                         ncols, tgt, s));
+    LAUNCH(rowstats_loss(md->losses, md->ce_lse, stats, ncols, ncols, tgt, targets, M, md->V,
+                         md->err_flag, s));
+  } else {  // fp32 or small shapes: the logits, then the loss alone
+    LAUNCH(gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
+                epi(EPI_STORE, md->logits, md->ldl), s));
+    LAUNCH(crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax, md->logits, md->ldl,
+                                targets, M, md->V, md->err_flag, s));
+  }
+  LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
+  md->have_targets = false;  // nothing for a backward
   return GPT2_OK;
 }
 
