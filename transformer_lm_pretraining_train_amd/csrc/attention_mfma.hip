@@ -70,19 +70,33 @@ __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ int acc_row(int r, int h2) { return 8 * (r / 4) + 4 * h2 + (r % 4); }
 
 // 64 rows x 64 columns of bf16 from global (row stride ld), rows >= nrows
-// read as zero: two 16-byte chunks per thread.
+// read as zero: two 16-byte chunks per thread, through a buffer resource
+// that starts at the tile's first row and ends with row nrows - 1, so the
+// hardware range check supplies the zeros (no per-load branch).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer (stride 0), 32-bit data format
 struct TileRegs {
   uint4 v[2];
 };
 __device__ __forceinline__ void tile_load(TileRegs& R, const bf16* __restrict__ src, int64_t ld,
                                           int row0, int nrows) {
+  const int rem = nrows - row0;
+  const int bytes = rem > 0 ? (int)(((int64_t)(rem - 1) * ld + HD) * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(src + (int64_t)row0 * ld), (short)0, bytes, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    int c = threadIdx.x + 256 * i;
-    int row = c / 8, d = (c % 8) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + row < nrows) v = *reinterpret_cast<const uint4*>(src + (int64_t)(row0 + row) * ld + d);
-    R.v[i] = v;
+    const int c = threadIdx.x + 256 * i;
+    const int row = c / 8, d = (c % 8) * 8;
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist only for the GPU target
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)((row * ld + d) * 2), 0, 0);
+    R.v[i] = make_uint4(w.x, w.y, w.z, w.w);
+#else
+    (void)rs;
+    (void)row;
+    (void)d;
+    R.v[i] = make_uint4(0, 0, 0, 0);
+#endif
   }
 }
 __device__ __forceinline__ void tile_store(const TileRegs& R, bf16* __restrict__ S) {
