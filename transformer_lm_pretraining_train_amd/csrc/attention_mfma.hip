@@ -410,9 +410,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     tile_load(rv, vbase, ld, TB, T);
   }
   __syncthreads();
-  // One 64-key tile for this wave's 32 queries; diag on the tiles that reach
-  // past the wave's first query.
-  auto dq_tile = [&](const bf16* Ks, const bf16* Vs, int k0, bool diag) {
+  // One 64-key tile for this wave's 32 queries; DIAG (a compile-time
+  // constant, so that the other tiles carry no masking code) on the tiles
+  // that reach past the wave's first query.
+  auto dq_tile = [&](auto diag_c, const bf16* Ks, const bf16* Vs, int k0) {
+    constexpr bool diag = decltype(diag_c)::value;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16_t s = zero16(), dp = zero16();
@@ -424,7 +426,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = exp2_(__builtin_fmaf(s[r], c, -L2));
-        if (diag && k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
+        if constexpr (diag) {
+          if (k0 + t * 32 + acc_row(r, h2) > myq) p = 0.f;
+        }
         s[r] = p * (dp[r] - Dq);  // dS^T
       }
 #pragma unroll
@@ -447,19 +451,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       }
     }
   };
-  // as in the forward: unconditional tiles first, then the block's last one
+  // Tiles wholly at or before every query of the block need no mask; then,
+  // as in the forward, the tiles every wave needs run unconditionally, and
+  // the block's last one only for the waves that reach it.
+  const int nfree = min(nkb, (q0 + 1) / TB);
   const int nall = min(nkb, (q0 + 31) / TB + 1);
   int kb = 0;
+  for (; kb < nfree; ++kb) {
+    const bf16* Ks = smem + (kb & 1) * 2 * TILE;
+    advance(kb);
+    dq_tile(std::false_type{}, Ks, Ks + TILE, kb * TB);
+    __syncthreads();
+  }
   for (; kb < nall; ++kb) {
     const bf16* Ks = smem + (kb & 1) * 2 * TILE;
     advance(kb);
-    dq_tile(Ks, Ks + TILE, kb * TB, kb * TB + TB - 1 > qw);
+    dq_tile(std::true_type{}, Ks, Ks + TILE, kb * TB);
     __syncthreads();
   }
   for (; kb < nkb; ++kb) {
     const bf16* Ks = smem + (kb & 1) * 2 * TILE;
     advance(kb);
-    if (kb * TB <= qw + 31) dq_tile(Ks, Ks + TILE, kb * TB, true);
+    if (kb * TB <= qw + 31) dq_tile(std::true_type{}, Ks, Ks + TILE, kb * TB);
     __syncthreads();
   }
   if (qvalid) {
@@ -525,10 +538,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       LD[stage][1][threadIdx.x] = dsv;
     }
   };
-  // One 64-query tile for this wave's 32 keys; diag on the tiles whose
-  // first queries precede some of the wave's keys.
-  auto dkv_tile = [&](const bf16* Qs, const bf16* Os, const float* Ls, const float* Ds, int qs0,
-                      bool diag) {
+  // One 64-query tile for this wave's 32 keys; DIAG (compile-time) on the
+  // tiles whose first queries precede some of the wave's keys.
+  auto dkv_tile = [&](auto diag_c, const bf16* Qs, const bf16* Os, const float* Ls,
+                      const float* Ds, int qs0) {
+    constexpr bool diag = decltype(diag_c)::value;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       f32x16_t s = zero16(), dp = zero16();
@@ -547,7 +561,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
           float p = exp2_(__builtin_fmaf(s[r], c, -Lv[j]));
-          if (diag && qs0 + rowb + j < mykey) p = 0.f;
+          if constexpr (diag) {
+            if (qs0 + rowb + j < mykey) p = 0.f;
+          }
           s[r] = p;
           dp[r] = p * (dp[r] - Dv[j]);  // dS
         }
@@ -570,20 +586,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   // iteration qb: stage tile qb+1, load qb+2, multiply tile qb.  Only the
   // first query tile (it starts at the block's first key) can be skipped by
-  // some waves; the rest run unconditionally, keeping the accumulators in place.
-  auto step = [&](int qb, bool need) {
+  // some waves; the rest run unconditionally, keeping the accumulators in
+  // place.  The first two tiles may hold queries before some of the block's
+  // keys and carry the mask; from the third on no query precedes a key.
+  auto step = [&](auto diag_c, int qb, bool need) {
     const int stage = (qb - qb0) & 1;
     const bf16* Qs = smem + stage * 2 * TILE;
     if (qb + 1 < nqb) {
       sstore(stage ^ 1);
       if (qb + 2 < nqb) gload(qb + 2);
     }
-    const int qs0 = qb * TB;
-    if (need) dkv_tile(Qs, Qs + TILE, LD[stage][0], LD[stage][1], qs0, qs0 < kw + 31);
+    if (need) dkv_tile(diag_c, Qs, Qs + TILE, LD[stage][0], LD[stage][1], qb * TB);
     __syncthreads();
   };
-  if (qb0 < nqb) step(qb0, qb0 * TB + TB - 1 >= kw);
-  for (int qb = qb0 + 1; qb < nqb; ++qb) step(qb, true);
+  static_assert(WQ == 2 * TB, "two masked query tiles per key block");
+  if (qb0 < nqb) step(std::true_type{}, qb0, qb0 * TB + TB - 1 >= kw);
+  if (qb0 + 1 < nqb) step(std::true_type{}, qb0 + 1, true);
+  for (int qb = qb0 + 2; qb < nqb; ++qb) step(std::false_type{}, qb, true);
   if (kvalid) {
     bf16* dst = dqkv + ((int64_t)b * T + mykey) * ld + hh * HD;
 #pragma unroll
