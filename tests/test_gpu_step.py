@@ -440,3 +440,52 @@ def test_forward_loss_without_logits_matches_forward(dtype, shape):
     orr = oracle_steps(ocfg, flat, [batches[0]])[0]
     tol = 1e-4 if dtype == "fp32" else 1e-2
     assert abs(float(lb) - orr["losses"][0]) <= tol * orr["losses"][0]
+
+
+def test_bf16_width_1600_matches_oracle():
+    """The GPT-2 1.5B width (25 heads of 64, C = 1600: the general LayerNorm
+    kernels, 4800- and 6400-wide products) in bf16 on a one-layer model."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "bf16", B=2, n_layer=1,
+                                                      n_embd=1600, n_head=25)
+    print("bf16 C=1600", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    assert abs(gs[0]["losses"][0] - orr["losses"][0]) <= 1e-2 * orr["losses"][0]
+    G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
+    for n in G:
+        assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+    assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-2
+
+
+def test_gpt2_1558m_shape_micro_step():
+    """One micro-step at the full GPT-2 1.5B shape (48 layers, C = 1600, 25
+    heads, T = 1024, Vp = 50304; B = 2 to keep it short): a loss near
+    ln(50257) at this initialisation, finite gradients, the evaluation
+    forward's loss, and recompute 2 reproducing the gradients bit for bit."""
+    wl = synth.workload("gpt2_1558m").replace(micro_batch=2, grad_accum=1)
+    layout = [(n, o, s) for n, o, s, _ in g.param_layout(g.config_for(wl, "bf16"))]
+    flat = synth.init_params(layout, wl.n_layer, wl.vocab_size, [wl.seed_id, 2])
+    stream = synth.token_stream(wl, wl.micro_batch * wl.seq_len + 1)
+    x, y = synth.micro_batch(stream, 0, wl.micro_batch, wl.seq_len)
+    xt, yt = to_dev(x), to_dev(y)
+    print("gpt2_1558m shape, B=2", flush=True)
+    grads = []
+    for r in (0, 2):
+        m = g.Model(g.config_for(wl, "bf16", recompute=r))
+        m.set_params(to_dev(flat))
+        m.zero_grad()
+        loss = torch.zeros(1, device="cuda")
+        m.forward(xt, yt, loss)
+        m.backward()
+        grads.append(host(m.get_grads()))
+        lval = float(loss)
+        if r == 0:
+            le = torch.zeros(1, device="cuda")
+            m.forward_loss(xt, yt, le)
+            assert float(le) == pytest.approx(lval, rel=1e-5)
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+        assert np.isfinite(lval) and abs(lval - np.log(wl.vocab_size)) < 0.5, lval
+    assert np.all(np.isfinite(grads[0])) and np.linalg.norm(grads[0]) > 0
+    assert np.array_equal(grads[0], grads[1])
