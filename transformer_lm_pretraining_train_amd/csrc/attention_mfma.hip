@@ -30,8 +30,12 @@
 //     column), P = exp(S - L), dS = P (dP - D), dV^T += dO^T P,
 //     dK^T += Q^T dS.
 // LDS is double-buffered (one barrier per tile) with the next tile's global
-// loads in flight during the current tile's math.  Workgroups of the causal
-// passes are issued longest-first.
+// loads (buffer loads whose range check zero-fills rows past T) in flight
+// during the current tile's math; the causal mask is compiled only into the
+// tiles that straddle the diagonal.  Workgroups of the causal passes are
+// issued longest-first.  Optionally each backward workgroup also sums the
+// columns of the dq / dk / dv rows it stores (the qkv bias gradient's first
+// stage).
 #include <type_traits>
 
 #include "common.h"

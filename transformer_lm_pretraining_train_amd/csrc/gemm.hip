@@ -8,15 +8,20 @@
 //   forward      y  = x W^T        A = x  (k-major), B = W  (k-major)
 //   input grad   dx = dy W         A = dy (k-major), B = W  (n-major)
 //   weight grad  dW += dy^T x      A = dy (m-major), B = x  (n-major)
-// and one kernel template covers all three with compile-time operand
-// orientation.  Operand tiles always land in LDS k-contiguous: a k-major
-// operand is copied with 16-byte vectors, an m/n-major one is read as
-// 4 k-rows x 8 columns per thread and transposed in registers before the
-// LDS store, so the MFMA fragment reads are single 16-byte LDS reads.
+// and each kernel template covers all three with compile-time operand
+// orientation.
 //
-// bf16: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  Workgroup tile
-// 128 x 128 x 64, four waves of 64 x 64 (2 x 2 MFMA tiles), next k-tile
-// prefetched into registers while the current one is multiplied.
+// bf16 (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   gemm_big_kernel -- the production path (M >= 256, N >= 128): 256 x
+//     {256, 192, 128} x 64 tiles, eight waves, operands streamed straight
+//     into two LDS stages by buffer loads, m/n-major operands read with
+//     transposing LDS reads, persistent or grouped (several products per
+//     launch), split-K with fixed-order reductions; epilogues staged through
+//     LDS (also the fc bias gradient's column sums and the head's softmax
+//     row statistics).  Described in detail further down.
+//   gemm_mfma_kernel -- small shapes: 128 x 128 x 64 tiles, four waves, the
+//     next k-tile prefetched into registers (m/n-major operands transposed
+//     in registers) while the current one is multiplied.
 // fp32 (the fp32 parity mode): plain LDS-tiled FMA kernel.
 #include <algorithm>
 #include <type_traits>
@@ -255,16 +260,18 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K,
 }
 
 // ================================================================ bf16 MFMA, large tiles
-// Workgroup tile BM x BN (256 x 256 or 256 x 128) x 64, four waves of
-// (BM/2) x (BN/2).  Two LDS stages: while the waves multiply stage s, the
-// next k-tile (already in registers) is written to stage s^1 and the one
-// after is fetched from global memory, with one barrier per k-tile.  LDS
-// rows are 64 bf16 (128 B) with the 16-byte chunks XOR-swizzled by row, so
-// both the fragment reads and the transposing stores stay (nearly) free of
-// bank conflicts.  Workgroups are mapped XCD-major, then in groups of 8
-// tile-rows, so that concurrently running tiles share operands in L2.
-// gridDim.y > 1 splits K; with EPI_PARTIAL each split writes its fp32 tile
-// to out + split * M * N and splitk_reduce adds them in order.
+// Workgroup tile BM x BN (BM = 256, BN = 256 / 192 / 128) x 64, eight waves
+// of (BM/4) x (BN/2).  Two LDS stages: while the waves multiply stage s,
+// the next k-tile streams into stage s^1 by buffer loads that write LDS
+// directly (BigOperand below), with one barrier per k-tile.  k-major
+// operands sit in LDS as 128-byte rows with XOR-swizzled 16-byte chunks;
+// m-major ones as they are in memory, read with ds_read_b64_tr_b16.
+// Persistent workgroups (one per CU) walk the tiles XCD-major in groups of 8
+// tile-rows, so that concurrently running tiles share operands in L2;
+// grouped launches give each workgroup one tile of one of several products.
+// gridDim.y > 1 (or a grouped split) divides K; with EPI_PARTIAL each split
+// writes its fp32 tile to out + split * M * N and the reduce kernels add
+// them in order.
 // Epilogue on 8 consecutive columns n .. n+7 of row m (16-byte accesses when
 // the row pitches allow it, element-wise at the ragged right edge).
 // res[j]: the value stored to out[m, n + j] as rounded (bf16 outputs; 0

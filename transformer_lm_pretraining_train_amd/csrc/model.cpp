@@ -1,6 +1,9 @@
 // Runtime of libgpt2.so: config validation, the flat parameter layout, the
 // carve-up of the caller's single workspace, and the launch sequences of
-// forward, backward and the optimizer step on one HIP stream.
+// forward, backward and the optimizer step on the caller's HIP stream (plus
+// one internal stream, joined by events, for the paired weight-gradient
+// launches of the backward); around the step, the loss-only forward, the
+// guarded optimizer step and checkpoint files.
 //
 // The whole model state lives in the one workspace the caller allocates, in
 // this order (each region 256-byte aligned): fp32 parameters, gradients,
