@@ -885,12 +885,15 @@ int64_t operand_span(bool kmajor, int rows, int K, int64_t ld) {
 
 template <int BM, int BN, int MODE>
 hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, int64_t lda,
-                      const bf16* b, int64_t ldb, const Epilogue& e, int splits, hipStream_t s) {
+                      const bf16* b, int64_t ldb, const Epilogue& e, int splits, hipStream_t s,
+                      bool persistent = true) {
   int tiles_m = (int)cdiv(M, BM), tiles_n = (int)cdiv(N, BN);
   int kps = (int)round_up(cdiv(K, splits), 64);
-  // one workgroup per CU (the LDS use allows no more), each looping over tiles
+  // one workgroup per CU (the LDS use allows no more), each looping over
+  // tiles; or one workgroup per tile, so that CUs that free up while another
+  // stream's kernel holds the rest keep taking tiles
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
-  const int g = (int)(splits > 1 ? ntiles : (ntiles < kCUs ? ntiles : kCUs));
+  const int g = (int)(splits > 1 || !persistent ? ntiles : (ntiles < kCUs ? ntiles : kCUs));
   dim3 grid((unsigned)g, (unsigned)splits);
   BigBatch batch{};
   batch.p[0] = BigProblem{M, N, tiles_m, tiles_n, a, lda, b, ldb, e};
@@ -909,7 +912,7 @@ hipError_t launch_big(bool akm, bool bkm, int M, int N, int K, const bf16* a, in
 template <int MODE>
 hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, const Epilogue& e, hipStream_t s, void* ws,
-                       size_t ws_bytes) {
+                       size_t ws_bytes, bool persistent) {
   if (dt == F32) {
     dim3 grid((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64));
     gemm_simt_kernel<MODE><<<grid, 256, 0, s>>>(akm, bkm, M, N, K, (const float*)A, lda,
@@ -953,10 +956,10 @@ hipError_t launch_mode(int dt, bool akm, bool bkm, int M, int N, int K, const vo
     }
   }
   if constexpr (big_square_ok(MODE)) {
-    if (p.kind == 1) return launch_big<256, 256, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
+    if (p.kind == 1) return launch_big<256, 256, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s, persistent);
   }
-  if (p.kind == 3) return launch_big<256, 192, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
-  return launch_big<256, 128, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s);
+  if (p.kind == 3) return launch_big<256, 192, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s, persistent);
+  return launch_big<256, 128, MODE>(akm, bkm, M, N, K, a, lda, b, ldb, e, 1, s, persistent);
 }
 
 }  // namespace
@@ -1134,7 +1137,7 @@ hipError_t gemm_rowstats(int M, int N, int K, const void* A, int64_t lda, const 
 
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
-                void* ws, size_t ws_bytes) {
+                void* ws, size_t ws_bytes, bool persistent) {
   if (e.colsum) {
     if (!gemm_colsum_ok(dt, a_kmajor, b_kmajor, M, N, K, lda, ldb, e.mode)) return hipErrorNotSupported;
     if (e.ldcs < N || e.ldcs % 2 != 0 || reinterpret_cast<uintptr_t>(e.colsum) % 8 != 0)
@@ -1144,16 +1147,16 @@ hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const
   if (dt == BF16 && (lda % 8 != 0 || ldb % 8 != 0)) return hipErrorInvalidValue;
   if (const int r = acc_row_split(dt, M, N, K, e.mode)) {
     hipError_t err = launch_mode<EPI_ACC_F32>(dt, a_kmajor, b_kmajor, r, N, K, A, lda, B, ldb, e, s,
-                                              ws, ws_bytes);
+                                              ws, ws_bytes, true);
     if (err != hipSuccess) return err;
     const bf16* A2 = (const bf16*)A + (a_kmajor ? (int64_t)r * lda : (int64_t)r);
     Epilogue e2 = e;
     e2.out = (float*)e.out + (int64_t)r * e.ldo;
     return launch_mode<EPI_ACC_F32>(dt, a_kmajor, b_kmajor, M - r, N, K, A2, lda, B, ldb, e2, s,
-                                    ws, ws_bytes);
+                                    ws, ws_bytes, true);
   }
 #define CASE(MD) \
-  case MD: return launch_mode<MD>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s, ws, ws_bytes);
+  case MD: return launch_mode<MD>(dt, a_kmajor, b_kmajor, M, N, K, A, lda, B, ldb, e, s, ws, ws_bytes, persistent);
   switch (e.mode) {
     CASE(EPI_STORE)
     CASE(EPI_BIAS)

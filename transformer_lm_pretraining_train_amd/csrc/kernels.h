@@ -121,9 +121,12 @@ struct Epilogue {
 // Split-K (used for fp32-accumulating products with few output tiles and a
 // long K) needs gemm_workspace_bytes() of scratch in `ws`.
 size_t gemm_workspace_bytes(int dt, int M, int N, int K, int mode);
+// persistent = false launches one workgroup per output tile instead of one
+// per CU looping over tiles: slower alone, but while another stream's kernel
+// holds most CUs the ones left free keep taking tiles.
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,
                 int64_t lda, const void* B, int64_t ldb, const Epilogue& e, hipStream_t s,
-                void* ws = nullptr, size_t ws_bytes = 0);
+                void* ws = nullptr, size_t ws_bytes = 0, bool persistent = true);
 // Whether gemm() can produce Epilogue::colsum for this product (it returns
 // hipErrorNotSupported for a colsum it cannot produce), and the number of
 // 64-row blocks it then writes.

@@ -757,7 +757,11 @@ int gpt2_backward(gpt2_model* md) {
       md->cols.back() = ColReduce{G + o.fc_b, nullptr, nullptr, slot, gemm_colsum_blocks(M),
                                   4 * C, 4 * C, 4 * C};
     }
-    LAUNCH(gemm(dt, true, false, M, 4 * C, C, in, C, md->wt(o.fcp_w), 4 * C, e, s));
+    // With weight-gradient pairs on the second stream (216 CUs each, often
+    // still running here), this product takes one workgroup per tile, so
+    // that the CUs the pair leaves free keep working through its tiles.
+    LAUNCH(gemm(dt, true, false, M, 4 * C, C, in, C, md->wt(o.fcp_w), 4 * C, e, s, nullptr, 0,
+                md->side == nullptr));
     // fc: fch = ln2 fc_w^T + fc_b  (d4 holds d fch)
     LAUNCH(gemm(dt, true, false, M, C, 4 * C, d4, 4 * C, md->wt(o.fc_w), C,
                 epi(EPI_STORE, md->dbuf_c, C), s));
