@@ -696,8 +696,11 @@ int gpt2_backward(gpt2_model* md) {
   // queued and launched together with the next layer's: one launch of eight
   // products when their tiles fit the chip in one round (else four at a
   // time).  Such a pair runs on the side stream, beside the next layer's
-  // work, except the last one; the main stream waits for it before it
-  // writes either of the pair's buffer sets again.
+  // work (the pair of the first two layers beside the embedding and the
+  // remaining bias and LayerNorm gradients); the main stream waits for it
+  // before it writes either of the pair's buffer sets again.  A pair that
+  // ends at layer 1 of an odd-depth model runs on the main stream, since the
+  // four products of layer 0 after it take the same split-K workspace.
   const int Lh = md->L;
   void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 3] : md->dres;
   int pend_pair = -1;  // pair running on the side stream whose sets are not yet reusable
@@ -807,7 +810,7 @@ int gpt2_backward(gpt2_model* md) {
     npend += 4;
     if (npend == 8) {
       if (gemm_acc_group_splits(dt, 8, pend, M) > 0) {  // both layers in one round of tiles
-        if (md->side && l > 1 && npairs < (int)md->ev_done.size()) {
+        if (md->side && l != 1 && npairs < (int)md->ev_done.size()) {
           // beside the next layer's work: the side stream starts once the
           // main stream has produced the inputs
           LAUNCH(hipEventRecord(md->ev_ready[npairs], s));
@@ -844,12 +847,13 @@ int gpt2_backward(gpt2_model* md) {
                                 &md->cols.back()));
     }
   }
-  // every weight gradient is in place before the backward returns
-  if (npairs > 0) LAUNCH(hipStreamWaitEvent(s, md->ev_done[npairs - 1], 0));
   LAUNCH(column_reduce_batched(md->cols.data(), (int)md->cols.size(), s));
   // embeddings
   LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
   LAUNCH(encoder_backward_wpe(dt, G + Ly.wpe, md->dres, md->B, md->Tn, C, s));
+  // every weight gradient is in place before the backward returns (the side
+  // stream's pairs write only the layers' matrices, none of the above)
+  if (npairs > 0) LAUNCH(hipStreamWaitEvent(s, md->ev_done[npairs - 1], 0));
   return GPT2_OK;
 }
 
