@@ -178,6 +178,22 @@ def test_small_bf16_step_matches_oracle():
     assert cosine(gr["v"], orr["v"]) > 0.98
 
 
+def test_small_bf16_odd_depth_matches_oracle():
+    """Five layers in bf16: the weight-gradient pair of layers 4-3 on the
+    second stream, of layers 2-1 on the main stream, layer 0's four products
+    alone after it."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("small", "bf16", k=2, n_layer=5)
+    print("small bf16, 5 layers, k=2", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    for a, b in zip(gs[0]["losses"], orr["losses"]):
+        assert abs(a - b) <= 1e-2 * abs(b)
+    G, O = per_tensor(layout, gs[0]["grads"]), per_tensor(layout, orr["grads"])
+    for n in G:
+        assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+    assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-2
+
+
 def test_tiny_bf16_step_matches_oracle():
     wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "bf16")
     _, gs = gpu_step(cfg, flat, batches)
