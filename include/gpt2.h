@@ -87,6 +87,21 @@ typedef struct {
                                 product from the kept pre-activation); 2 also the two
                                 LayerNorm outputs of each block (rerun from the kept block
                                 inputs).  Results are bit-identical across the three. */
+  int32_t fused_head;        /* 0: the forward stores the B*T x Vp logits and, with the loss,
+                                their gradient (2 x 1.65 GB at GPT-2 124M, B x T = 16 x 1024).
+                                1: neither is ever stored (the fused classifier carried to the
+                                head's products; dszhyy.com llm.c 1.5B post, PyTorch-comparison
+                                section): the forward takes the loss from per-row softmax
+                                statistics of the head's product, and the backward
+                                recomputes the product 4608 vocabulary columns at a time,
+                                turning each block straight into its logit gradient for the
+                                two gradient products (one more head-sized product per
+                                micro-step).  Needs bf16, padded_vocab_size a multiple of 64
+                                and >= 256, micro_batch * seq_len >= 256; then gpt2_forward
+                                requires targets and GPT2_DBG_LOGITS / GPT2_DBG_ARGMAX
+                                return GPT2_EINVAL.  The gradients match mode 0's to bf16
+                                rounding (not bit for bit: the log-sum-exp is combined in
+                                another order). */
 } gpt2_config;
 
 typedef struct {
@@ -157,7 +172,10 @@ int gpt2_forward_loss(gpt2_model* model, const int32_t* dev_tokens, const int32_
 /* Backward pass of the last forward (which must have had targets):
  * gradients += d(mean loss / k) / d params.  The logit gradient comes from
  * the forward's cross-entropy (computed with the loss, from the same read of
- * the logits); the logits themselves are left as the forward wrote them. */
+ * the logits); the logits themselves are left as the forward wrote them.
+ * With fused_head = 1 it is regenerated here instead (see gpt2_config).
+ * The forward's dev_tokens are read again here (the embedding gradient);
+ * its targets are kept by the model. */
 int gpt2_backward(gpt2_model* model);
 
 /* Gradients = 0. */

@@ -79,6 +79,28 @@ def test_recompute_shrinks_the_workspace():
     assert nb[1] - nb[2] == pytest.approx((2 * L - 7) * M * C * es, rel=1e-4)
 
 
+def test_fused_head_drops_the_logits():
+    """fused_head = 1 keeps neither the logits nor their gradient (2 x B*T x
+    round_up(Vp, 64) bf16) but a 4608-column block of the logit gradient, an
+    fp32 d lnf and the targets: 3.3 GB less at GPT-2 124M, B x T = 16 x 1024."""
+    wl = synth.workload("gpt2_124m")
+    nb = [g.workspace_bytes(g.config_for(wl, fused_head=f)) for f in (0, 1)]
+    M, C, ldl = wl.micro_batch * wl.seq_len, wl.n_embd, 50304
+    kept = 2 * M * ldl * 2 - (M * 4608 * 2 + M * C * 4 + M * 4)
+    assert abs((nb[0] - nb[1]) - kept) <= 64 * 2 ** 20, (nb[0] - nb[1], kept)
+
+
+@pytest.mark.parametrize("over,ok", [
+    (dict(padded_vocab_size=320), True),
+    (dict(padded_vocab_size=300), False),    # not a multiple of 64
+    (dict(padded_vocab_size=128), False),    # fewer than 256 columns
+    (dict(padded_vocab_size=320, micro_batch=2), False)])  # 128 rows
+def test_fused_head_shape_limits(over, ok):
+    wl = synth.workload("tiny").replace(**over)
+    cfg = g.config_for(wl, "bf16", fused_head=1)
+    assert (g.lib().gpt2_workspace_bytes(ctypes.byref(cfg)) > 0) == ok
+
+
 def test_deterministic_flag_accepted():
     cfg = g.config_for(synth.workload("tiny"))
     cfg.deterministic = 1
@@ -87,7 +109,8 @@ def test_deterministic_flag_accepted():
 
 @pytest.mark.parametrize("field,value", [
     ("n_embd", 100), ("n_head", 7), ("seq_len", 2048), ("padded_vocab_size", 10),
-    ("dtype", 5), ("micro_batch", 0), ("ln_eps", 0.0), ("recompute", 3), ("recompute", -1)])
+    ("dtype", 5), ("micro_batch", 0), ("ln_eps", 0.0), ("recompute", 3), ("recompute", -1),
+    ("fused_head", 2), ("fused_head", -1), ("fused_head", 1)])  # the last: fp32
 def test_invalid_configs_rejected(field, value):
     cfg = g.config_for(synth.workload("tiny"))
     setattr(cfg, field, value)

@@ -554,3 +554,77 @@ def test_gpt2_124m_full_size_sampled_sequences_match_oracle():
         print(f"sequence {b}: loss {gl.mean():.5f} vs {ol.mean():.5f}, "
               f"max |d loss| {np.abs(gl - ol).max():.4f}, min lnf cosine {cos.min():.5f}",
               flush=True)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=8, n_layer=1, vocab_size=300, padded_vocab_size=320),  # one block, a ragged tile
+    dict(B=4, n_layer=1, n_embd=768, n_head=12, vocab_size=50257, padded_vocab_size=50304)])
+def test_fused_head_matches_oracle_and_stored_logits(shape):
+    """fused_head = 1 (no logits stored; the backward regenerates their
+    gradient per 4608-column block): the step matches the oracle to the bf16
+    bars, and the gradients of the path that stores the logits to bf16
+    rounding (cosine >= 0.9999 per tensor, same loss to 1e-5)."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "bf16", k=2, **shape)
+    print(f"fused head, {shape}", flush=True)
+    _, ref = gpu_step(cfg, flat, batches)
+    cfg.fused_head = 1
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    for a, b, c in zip(gs[0]["losses"], ref[0]["losses"], orr["losses"]):
+        assert abs(a - b) <= 1e-5 * b
+        assert abs(a - c) <= 1e-2 * c
+    G, R, O = (per_tensor(layout, x["grads"]) for x in (gs[0], ref[0], orr))
+    for n in G:
+        assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+        assert cosine(G[n], R[n]) >= 0.9999, (n, cosine(G[n], R[n]))
+    assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-2
+
+
+def test_fused_head_keeps_no_logits():
+    wl, cfg, ocfg, layout, flat, batches = setup_case(
+        "tiny", "bf16", B=8, n_layer=1, vocab_size=300, padded_vocab_size=320)
+    cfg.fused_head = 1
+    m = g.Model(cfg)
+    m.set_params(to_dev(flat))
+    x, y = to_dev(batches[0][0]), to_dev(batches[0][1])
+    with pytest.raises(g.GPT2Error) as ei:
+        m.forward(x, None, None)
+    assert ei.value.name == "EINVAL"
+    m.forward(x, y, None)
+    buf = torch.empty(x.numel() * 320, dtype=torch.bfloat16, device="cuda")
+    for name in ("logits", "argmax"):
+        with pytest.raises(g.GPT2Error) as ei:
+            m.debug_read(name, buf)
+        assert ei.value.name == "EINVAL"
+    m.backward()
+    torch.cuda.synchronize()
+
+
+def test_gpt2_124m_full_size_fused_head_matches_stored_logits():
+    """The 124M configuration at its full micro-batch (bf16, B = 16, T =
+    1024): one micro-step with fused_head = 1 against the same micro-step
+    storing the logits -- same loss to 1e-5, per-tensor gradient cosine >=
+    0.9999."""
+    wl = synth.workload("gpt2_124m").replace(grad_accum=1)
+    layout = [(n, o, s) for n, o, s, _ in g.param_layout(g.config_for(wl, "bf16"))]
+    flat = synth.init_params(layout, wl.n_layer, wl.vocab_size, [wl.seed_id, 2])
+    stream = synth.token_stream(wl, wl.micro_batch * wl.seq_len + 1)
+    x, y = synth.micro_batch(stream, 0, wl.micro_batch, wl.seq_len)
+    xt, yt = to_dev(x), to_dev(y)
+    print("gpt2_124m full micro-batch, fused head vs stored logits", flush=True)
+    out = []
+    for f in (0, 1):
+        m = g.Model(g.config_for(wl, "bf16", fused_head=f))
+        m.set_params(to_dev(flat))
+        m.zero_grad()
+        loss = torch.zeros(1, device="cuda")
+        m.forward(xt, yt, loss)
+        m.backward()
+        out.append((float(loss), host(m.get_grads())))
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+    assert abs(out[1][0] - out[0][0]) <= 1e-5 * out[0][0]
+    G, R = per_tensor(layout, out[1][1]), per_tensor(layout, out[0][1])
+    for n in G:
+        assert cosine(G[n], R[n]) >= 0.9999, (n, cosine(G[n], R[n]))

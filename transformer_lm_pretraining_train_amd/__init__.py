@@ -39,7 +39,7 @@ class GPT2Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layer", "n_head", "n_embd", "block_size", "vocab_size", "padded_vocab_size",
         "micro_batch", "seq_len", "grad_accum_steps", "dtype", "deterministic")] + [
-        ("ln_eps", ctypes.c_float), ("recompute", ctypes.c_int32)]
+        ("ln_eps", ctypes.c_float), ("recompute", ctypes.c_int32), ("fused_head", ctypes.c_int32)]
 
     def __repr__(self):
         return "GPT2Config(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"

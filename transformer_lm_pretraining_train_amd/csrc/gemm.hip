@@ -51,6 +51,12 @@ __device__ __forceinline__ float epi_apply(const Epilogue& e, int m, int n, floa
     // GELU of the stored (rounded) pre-activation, so that the backward,
     // which differentiates at the stored value, is consistent with it.
     ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(to_f(y)));
+  } else if constexpr (MODE == EPI_DLOGITS) {
+    const int c = e.col0 + n;
+    const int yy = min(max(e.targets[m], 0), e.vocab - 1);
+    float p = c < e.vocab ? fast_exp(to_f(from_f<T>(acc)) - e.lse[m]) : 0.f;
+    if (c == yy) p -= 1.f;
+    y = from_f<T>(p * e.scale);
   } else if constexpr (MODE == EPI_GELU_BWD) {
     float h = to_f(((const T*)e.aux)[(int64_t)m * e.ldx + n]);
     y = from_f<T>(acc * gelu_grad_f(h));
@@ -316,6 +322,17 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
         Pack<bf16> r = load_pack((const bf16*)e.resid + (int64_t)m * e.ldr + n);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] += to_f(r.e[j]);
+      }
+      if constexpr (MODE == EPI_DLOGITS) {
+        // the cross-entropy's gradient of the logits z = bf16(acc)
+        const float l = e.lse[m];
+        const int yy = min(max(e.targets[m], 0), e.vocab - 1) - e.col0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float p = e.col0 + n + j < e.vocab ? fast_exp((float)(bf16)x[j] - l) : 0.f;
+          if (n + j == yy) p -= 1.f;
+          x[j] = p * e.scale;
+        }
       }
       if constexpr (MODE == EPI_GELU_BWD) {
         Pack<bf16> h = load_pack((const bf16*)e.aux + (int64_t)m * e.ldx + n);
@@ -1133,6 +1150,28 @@ hipError_t gemm_rowstats(int M, int N, int K, const void* A, int64_t lda, const 
   gemm_big_kernel<256, 256, true, true, EPI_ROWSTATS><<<grid, BIG_THREADS, 0, s>>>(
       batch, K, (int)round_up(K, 64));
   return hipGetLastError();
+}
+
+bool gemm_dlogits_ok(int dt, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldo) {
+  return gemm_rowstats_ok(dt, M, N, K, lda, ldb) && ldo % 8 == 0 && ldo >= N;
+}
+
+hipError_t gemm_dlogits(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, const float* lse, const int32_t* targets, int col0, int V,
+                        float scale, void* out, int64_t ldo, hipStream_t s) {
+  if (!gemm_dlogits_ok(BF16, M, N, K, lda, ldb, ldo)) return hipErrorNotSupported;
+  if (V < 1 || col0 < 0 || !lse || !targets || !out) return hipErrorInvalidValue;
+  Epilogue e{};
+  e.mode = EPI_DLOGITS;
+  e.out = out;
+  e.ldo = ldo;
+  e.lse = lse;
+  e.targets = targets;
+  e.col0 = col0;
+  e.vocab = V;
+  e.scale = scale;
+  return launch_big<256, 192, EPI_DLOGITS>(true, true, M, N, K, (const bf16*)A, lda,
+                                           (const bf16*)B, ldb, e, 1, s);
 }
 
 hipError_t gemm(int dt, bool a_kmajor, bool b_kmajor, int M, int N, int K, const void* A,

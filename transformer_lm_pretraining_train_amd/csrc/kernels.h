@@ -97,7 +97,8 @@ enum EpiMode {
   EPI_GELU_BWD = 4,    // out = acc * gelu'(aux[m, n]); out2 (if not null) = gelu(aux[m, n])
   EPI_ACC_F32 = 5,     // out (fp32) += acc
   EPI_PARTIAL = 6,     // internal: split-K partial tile, fp32
-  EPI_ROWSTATS = 7     // internal: softmax row statistics, see gemm_rowstats()
+  EPI_ROWSTATS = 7,    // internal: softmax row statistics, see gemm_rowstats()
+  EPI_DLOGITS = 8      // internal: cross-entropy logit gradient, see gemm_dlogits()
 };
 struct Epilogue {
   int mode;
@@ -117,6 +118,11 @@ struct Epilogue {
   // order.
   float* colsum;
   int64_t ldcs;
+  // EPI_DLOGITS only: column n of the product is vocabulary entry col0 + n.
+  const float* lse;
+  const int32_t* targets;
+  int col0, vocab;
+  float scale;
 };
 // Split-K (used for fp32-accumulating products with few output tiles and a
 // long K) needs gemm_workspace_bytes() of scratch in `ws`.
@@ -152,6 +158,18 @@ hipError_t gemm_rowstats(int M, int N, int K, const void* A, int64_t lda, const 
 hipError_t rowstats_loss(float* losses, float* lse, const float2* stats, int64_t ld, int ncols,
                          const float* tgt, const int32_t* targets, int M, int V, int* err_flag,
                          hipStream_t s);
+// The gradient of the mean cross-entropy for one block of vocabulary
+// columns without the logits in memory: z = bf16(A B^T) for rows m < M and
+// the N columns n of B (B = rows col0 .. col0 + N - 1 of the tied head; A,
+// B k-major), then out[m * ldo + n] = bf16(scale * (exp(z - lse[m]) -
+// [col0 + n == y])) with y = targets[m] clamped to [0, V), and 0 where
+// col0 + n >= V -- what the cross-entropy computes from the stored logits.
+// Only bf16 products on the large tiles (gemm_dlogits_ok: also ldo a
+// multiple of 8).
+bool gemm_dlogits_ok(int dt, int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldo);
+hipError_t gemm_dlogits(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                        int64_t ldb, const float* lse, const int32_t* targets, int col0, int V,
+                        float scale, void* out, int64_t ldo, hipStream_t s);
 // out (fp32, pitch ldo) += sum_k A[k * lda + m] B[k * ldb + n] for m < M,
 // n < N: a weight gradient dW += dy^T x with dy and x stored row-major.
 struct AccItem {

@@ -105,6 +105,11 @@ Layout make_layout(const gpt2_config& c) {
   return L;
 }
 
+// fused_head: the backward regenerates the logit gradient this many
+// vocabulary columns at a time (24 tiles of 192 columns; 151 MB at
+// B x T = 16 x 1024)
+constexpr int kHeadChunk = 4608;
+
 int validate(const gpt2_config* c) {
   if (!c) return fail(GPT2_EINVAL, "config is NULL");
   if (c->n_layer < 1 || c->n_head < 1) return fail(GPT2_EINVAL, "n_layer and n_head must be >= 1");
@@ -125,6 +130,17 @@ int validate(const gpt2_config* c) {
   if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16) return fail(GPT2_EINVAL, "dtype must be 0 or 1");
   if (!(c->ln_eps > 0.f)) return fail(GPT2_EINVAL, "ln_eps must be > 0");
   if (c->recompute < 0 || c->recompute > 2) return fail(GPT2_EINVAL, "recompute must be 0, 1 or 2");
+  if (c->fused_head < 0 || c->fused_head > 1) return fail(GPT2_EINVAL, "fused_head must be 0 or 1");
+  if (c->fused_head) {
+    const int64_t M = (int64_t)c->micro_batch * c->seq_len;
+    if (c->dtype != GPT2_BF16) return fail(GPT2_EINVAL, "fused_head needs dtype bf16");
+    if (c->padded_vocab_size % 64 != 0)
+      return fail(GPT2_EINVAL, "fused_head needs padded_vocab_size a multiple of 64");
+    if (!gemm_rowstats_ok(BF16, (int)M, c->padded_vocab_size, c->n_embd, c->n_embd, c->n_embd) ||
+        !gemm_dlogits_ok(BF16, (int)M, std::min(c->padded_vocab_size, kHeadChunk), c->n_embd,
+                         c->n_embd, c->n_embd, kHeadChunk))
+      return fail(GPT2_EINVAL, "fused_head needs micro_batch * seq_len >= 256 and padded_vocab_size >= 256");
+  }
   return GPT2_OK;
 }
 
@@ -154,6 +170,15 @@ struct gpt2_model {
   float *lnf_mean, *lnf_rstd;
   void* logits;
   void* dlogits;  // d loss / d logits of the last forward with targets (same pitch)
+  // fused_head: no logits or dlogits (both null); the backward regenerates
+  // d logits per block of kHeadChunk vocabulary columns into head_chunk
+  // (pitch head_ld), which the forward's row statistics also use, and sums
+  // d lnf over the blocks in fp32 (dlnf32)
+  bool fused_head = false;
+  void* head_chunk = nullptr;
+  int64_t head_ld = 0;
+  float* dlnf32 = nullptr;
+  int32_t* targets_keep = nullptr;  // the forward's targets, for the backward
   float *losses, *ce_lse, *loss_internal;
   int32_t* argmax;
   // backward
@@ -268,8 +293,18 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.lnf = cv.take(M * C * es);
   md.lnf_mean = (float*)cv.take(M * 4);
   md.lnf_rstd = (float*)cv.take(M * 4);
-  md.logits = cv.take(M * ldl * es);
-  md.dlogits = cv.take(M * ldl * es);
+  md.fused_head = c.fused_head != 0;
+  if (md.fused_head) {
+    md.logits = md.dlogits = nullptr;
+    md.head_ld = std::min<int64_t>(c.padded_vocab_size, kHeadChunk);
+    const int64_t ncols = gemm_rowstats_cols(c.padded_vocab_size);
+    md.head_chunk = cv.take(std::max<int64_t>(M * md.head_ld * es, round_up(M * ncols * 8, 256) + M * 4));
+    md.dlnf32 = (float*)cv.take(M * C * 4);
+    md.targets_keep = (int32_t*)cv.take(M * 4);
+  } else {
+    md.logits = cv.take(M * ldl * es);
+    md.dlogits = cv.take(M * ldl * es);
+  }
   md.losses = (float*)cv.take(M * 4);
   md.ce_lse = (float*)cv.take(M * 4);
   md.argmax = (int32_t*)cv.take(M * 4);
@@ -301,6 +336,11 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
     const int dWshapes[5][2] = {{c.padded_vocab_size, Ci}, {Ci, 4 * Ci}, {4 * Ci, Ci}, {Ci, Ci},
                                 {3 * Ci, Ci}};
     for (auto& sh : dWshapes) gw = std::max(gw, gemm_workspace_bytes(dt, sh[0], sh[1], Mi, EPI_ACC_F32));
+    if (c.fused_head) {  // the head's gradient per block of vocabulary rows
+      const int Vp = c.padded_vocab_size;
+      gw = std::max(gw, gemm_workspace_bytes(dt, std::min(Vp, kHeadChunk), Ci, Mi, EPI_ACC_F32));
+      if (Vp % kHeadChunk) gw = std::max(gw, gemm_workspace_bytes(dt, Vp % kHeadChunk, Ci, Mi, EPI_ACC_F32));
+    }
     // the four weight gradients of a layer as one launch (shapes and pitches only)
     const AccItem grp[4] = {{Ci, 4 * Ci, nullptr, Ci, nullptr, 4 * Ci, nullptr, 4 * Ci},
                             {4 * Ci, Ci, nullptr, 4 * Ci, nullptr, Ci, nullptr, Ci},
@@ -600,13 +640,43 @@ static int forward_trunk(gpt2_model* md, const int32_t* tokens, const int32_t* t
   return GPT2_OK;
 }
 
+// The loss of the tied head from per-row softmax statistics of its product,
+// never the logits (bf16, shapes gemm_rowstats_ok() accepts): per-row (max,
+// sum) of every 128 logits and the target's logit into `work`, then
+// log-sum-exp and loss per row, then the mean.
+static int head_loss_rowstats(gpt2_model* md, const int32_t* targets, void* work,
+                              float* dev_loss) {
+  const int C = md->C, M = (int)md->M;
+  hipStream_t s = md->stream;
+  const int ncols = gemm_rowstats_cols(md->Vp);
+  float2* stats = (float2*)work;
+  float* tgt = (float*)((char*)work + round_up((int64_t)M * ncols * 8, 256));
+  LAUNCH(gemm_rowstats(M, md->Vp, C, md->lnf, C, md->wt(md->lay.wte), C, md->V, targets, stats,
+                       ncols, tgt, s));
+  LAUNCH(rowstats_loss(md->losses, md->ce_lse, stats, ncols, ncols, tgt, targets, M, md->V,
+                       md->err_flag, s));
+  LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
+  return GPT2_OK;
+}
+
 int gpt2_forward(gpt2_model* md, const int32_t* tokens, const int32_t* targets, float* dev_loss) {
+  if (md && md->fused_head && !targets)
+    return fail(GPT2_EINVAL, "fused_head keeps no logits: gpt2_forward needs targets");
   const int rc = forward_trunk(md, tokens, targets);
   if (rc != GPT2_OK) return rc;
   const int dt = md->dt;
   const int C = md->C, M = (int)md->M;
   const Layout& Ly = md->lay;
   hipStream_t s = md->stream;
+  if (md->fused_head) {
+    // the loss from row statistics; the backward regenerates d logits from
+    // the log-sum-exp and these targets
+    LAUNCH(hipMemcpyAsync(md->targets_keep, targets, (size_t)M * 4, hipMemcpyDeviceToDevice, s));
+    const int r = head_loss_rowstats(md, targets, md->head_chunk, dev_loss);
+    if (r != GPT2_OK) return r;
+    md->have_targets = true;
+    return GPT2_OK;
+  }
   // logits over the padded vocabulary (tied head: wte)
   TIMED(GPT2_TIMER_LM_HEAD_FWD, gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
                                      epi(EPI_STORE, md->logits, md->ldl), s));
@@ -630,25 +700,19 @@ int gpt2_forward_loss(gpt2_model* md, const int32_t* tokens, const int32_t* targ
   const int dt = md->dt, C = md->C, M = (int)md->M;
   const Layout& Ly = md->lay;
   hipStream_t s = md->stream;
-  if (gemm_rowstats_ok(dt, M, md->Vp, C, C, C)) {
-    // per-row (max, sum) of every 128 logits and the target's logit, never
-    // the logits themselves; the gradient buffer (unused without a
-    // backward) holds them
-    const int ncols = gemm_rowstats_cols(md->Vp);
-    float2* stats = (float2*)md->dlogits;
-    float* tgt = (float*)((char*)md->dlogits + round_up((int64_t)M * ncols * 8, 256));
-    LAUNCH(gemm_rowstats(M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C, md->V, targets, stats,
-                         ncols, tgt, s));
-    LAUNCH(rowstats_loss(md->losses, md->ce_lse, stats, ncols, ncols, tgt, targets, M, md->V,
-                         md->err_flag, s));
-  } else {  // fp32 or small shapes: the logits, then the loss alone
-    LAUNCH(gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
-                epi(EPI_STORE, md->logits, md->ldl), s));
-    LAUNCH(crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax, md->logits, md->ldl,
-                                targets, M, md->V, md->err_flag, s));
-  }
-  LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
   md->have_targets = false;  // nothing for a backward
+  if (gemm_rowstats_ok(dt, M, md->Vp, C, C, C)) {
+    // the gradient buffer (unused without a backward), or the fused head's
+    // chunk buffer, holds the row statistics
+    return head_loss_rowstats(md, targets, md->fused_head ? md->head_chunk : md->dlogits,
+                              dev_loss);
+  }
+  // fp32 or small shapes: the logits, then the loss alone
+  LAUNCH(gemm(dt, true, true, M, md->Vp, C, md->lnf, C, md->wt(Ly.wte), C,
+              epi(EPI_STORE, md->logits, md->ldl), s));
+  LAUNCH(crossentropy_forward(dt, md->losses, md->ce_lse, md->argmax, md->logits, md->ldl,
+                              targets, M, md->V, md->err_flag, s));
+  LAUNCH(mean_loss(dev_loss ? dev_loss : md->loss_internal, md->losses, M, s));
   return GPT2_OK;
 }
 
@@ -681,11 +745,31 @@ int gpt2_backward(gpt2_model* md) {
     md->cols.emplace_back();
     return p;
   };
-  // tied head (d logits from the forward's cross-entropy): dwte += dz^T lnf ; dlnf = dz wte
-  LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->dlogits, md->ldl, md->lnf, C,
-              epi(EPI_ACC_F32, G + Ly.wte, C), s, md->gemm_ws, md->gemm_ws_bytes));
-  LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->dlogits, md->ldl, md->wt(Ly.wte), C,
-              epi(EPI_STORE, md->dbuf_c, C), s));
+  if (md->fused_head) {
+    // tied head without stored logits: per block of vocabulary columns,
+    // d logits regenerated from lnf, wte and the forward's log-sum-exp, then
+    // d lnf += dz wte (fp32 over the blocks) and dwte += dz^T lnf
+    const float seed = (float)(1.0 / ((double)md->M * md->k));
+    LAUNCH(fill_f32(md->dlnf32, 0.f, (int64_t)M * C, s));
+    for (int col0 = 0; col0 < md->Vp; col0 += kHeadChunk) {
+      const int nc = std::min(kHeadChunk, md->Vp - col0);
+      const void* wc = (const char*)md->wt(Ly.wte) + (int64_t)col0 * C * dsize(dt);
+      LAUNCH(gemm_dlogits(M, nc, C, md->lnf, C, wc, C, md->ce_lse, md->targets_keep, col0, md->V,
+                          seed, md->head_chunk, md->head_ld, s));
+      LAUNCH(gemm(dt, true, false, M, C, nc, md->head_chunk, md->head_ld, wc, C,
+                  epi(EPI_ACC_F32, md->dlnf32, C), s));
+      LAUNCH(gemm(dt, false, false, nc, C, M, md->head_chunk, md->head_ld, md->lnf, C,
+                  epi(EPI_ACC_F32, G + Ly.wte + (int64_t)col0 * C, C), s, md->gemm_ws,
+                  md->gemm_ws_bytes));
+    }
+    LAUNCH(cast_f32_to_bf16(md->dbuf_c, md->dlnf32, (int64_t)M * C, s));
+  } else {
+    // tied head (d logits from the forward's cross-entropy): dwte += dz^T lnf ; dlnf = dz wte
+    LAUNCH(gemm(dt, false, false, md->Vp, C, M, md->dlogits, md->ldl, md->lnf, C,
+                epi(EPI_ACC_F32, G + Ly.wte, C), s, md->gemm_ws, md->gemm_ws_bytes));
+    LAUNCH(gemm(dt, true, false, M, C, md->Vp, md->dlogits, md->ldl, md->wt(Ly.wte), C,
+                epi(EPI_STORE, md->dbuf_c, C), s));
+  }
   const void* xfinal = md->L > 0 ? md->act[md->L - 1].res3 : md->encoded;
   // The column sums of each residual gradient a LayerNorm backward produces
   // are the bias gradient of the linear layer that wrote that residual:
@@ -1126,9 +1210,17 @@ int gpt2_debug_read(gpt2_model* md, int which, int layer, void* dst, size_t byte
   size_t n = 0;
   auto need_layer = [&]() { return layer >= 0 && layer < md->L; };
   switch (which) {
-    case GPT2_DBG_LOGITS: src = md->logits; n = M * md->ldl * es; break;
+    case GPT2_DBG_LOGITS:
+      if (!md->logits) return fail(GPT2_EINVAL, "fused_head keeps no logits");
+      src = md->logits;
+      n = M * md->ldl * es;
+      break;
     case GPT2_DBG_LOSSES: src = md->losses; n = M * 4; break;
-    case GPT2_DBG_ARGMAX: src = md->argmax; n = M * 4; break;
+    case GPT2_DBG_ARGMAX:
+      if (md->fused_head) return fail(GPT2_EINVAL, "fused_head computes no argmax");
+      src = md->argmax;
+      n = M * 4;
+      break;
     case GPT2_DBG_ACT_LNF: src = md->lnf; n = M * C * es; break;
     case GPT2_DBG_ENCODED: src = md->encoded; n = M * C * es; break;
     case GPT2_DBG_ACT_LN1:
