@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0
 # counters read for a plain 1 GiB device copy (FETCH_SIZE reads half the
 # bytes copied: factor 2.0; WRITE_SIZE is exact: factor 1.0).  Valid only for
 # the GEMM source it was measured on (first 16 hex digits of its sha256).
-LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "c06e7381debd1b43", "fetch_kib": 917457, "write_kib": 1609728,
+LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "9d1ce4d98e8db783", "fetch_kib": 918140, "write_kib": 1609728,
                    "fetch_factor": 2.0, "write_factor": 1.0}
 
 
