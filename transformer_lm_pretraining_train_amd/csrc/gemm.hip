@@ -678,17 +678,22 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
   // 32 rows, then over the wave's TI row blocks -- the wave's WM = 64 rows,
   // one colsum block.
   // Softmax row statistics (EPI_ROWSTATS): lane l of a 256-column tile
-  // handles rows l/8 + 8t (t < 4) of the slab and columns 8 (l%8) .. +8; the
-  // eight lanes of a row combine their (max, sum) by shuffles, and across
-  // the wave's two column rounds, into one entry per row and 128 columns.
+  // handles rows l/8 + 8t (t < 4) of the slab and columns 8 (l%8) .. +8; it
+  // keeps one running (max, sum) per row over the wave's two column rounds,
+  // and the eight lanes of a row then combine theirs by shuffles, into one
+  // entry per row and 128 columns.
   constexpr bool kStats = MODE == EPI_ROWSTATS;
   static_assert(!kStats || (BN == 256 && JB == 2), "row statistics need 256-column tiles");
   float rmax[kStats ? 4 : 1], rsum[kStats ? 4 : 1];
+  // (m1, s1) <- the pair for the union of both sets; only the smaller
+  // maximum's sum needs rescaling (the other factor is exp(0) = 1)
   auto combine = [](float& m1, float& s1, float m2, float s2) {
-    const float m = fmaxf(m1, m2);
-    if (m == -INFINITY) return;  // both empty
-    s1 = s1 * fast_exp(m1 - m) + s2 * fast_exp(m2 - m);
-    m1 = m;
+    const bool first = m1 >= m2;
+    const float big = first ? m1 : m2, small = first ? m2 : m1;
+    if (big == -INFINITY) return;  // both empty
+    const float sbig = first ? s1 : s2, ssmall = first ? s2 : s1;
+    s1 = sbig + ssmall * fast_exp(small - big);
+    m1 = big;
   };
   constexpr bool kColsum = MODE == EPI_GELU_BWD;
   static_assert(!kColsum || WM == 64, "colsum blocks are the waves' 64 rows");
@@ -746,10 +751,7 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
             const int y = min(max(((const int32_t*)e.aux)[m], 0), V - 1);
             if (y >= n && y < n + 8) ((float*)e.out2)[m] = z[y - n];
           }
-#pragma unroll
-          for (int o = 1; o < 8; o <<= 1)
-            combine(cm, cs, __shfl_xor(cm, o, 64), __shfl_xor(cs, o, 64));
-          combine(rmax[t], rsum[t], cm, cs);
+          combine(rmax[t], rsum[t], cm, cs);  // this lane's columns; lanes combine below
           continue;
         }
         float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -774,6 +776,12 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
       __builtin_amdgcn_wave_barrier();
     }
     if constexpr (kStats) {
+      // the eight lanes of each row combine their running statistics
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1)
+          combine(rmax[t], rsum[t], __shfl_xor(rmax[t], o, 64), __shfl_xor(rsum[t], o, 64));
       if (lane % 8 == 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
