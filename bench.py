@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0
 # counters read for a plain 1 GiB device copy (FETCH_SIZE reads half the
 # bytes copied: factor 2.0; WRITE_SIZE is exact: factor 1.0).  Valid only for
 # the GEMM source it was measured on (first 16 hex digits of its sha256).
-LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "9d1ce4d98e8db783", "fetch_kib": 918140, "write_kib": 1609728,
+LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "361b88f5cfbbed5c", "fetch_kib": 921361, "write_kib": 1609728,
                    "fetch_factor": 2.0, "write_factor": 1.0}
 
 
@@ -50,6 +50,11 @@ def parse():
                     help="override k (micro-steps per optimizer step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--fused-head", action="store_true",
+                    help="train without stored logits (gpt2_config.fused_head = 1); no "
+                         "roofline entry, since the lm_head product it reports does not run")
+    ap.add_argument("--recompute", type=int, default=0, choices=(0, 1, 2),
+                    help="activation recompute (gpt2_config.recompute)")
     ap.add_argument("--cpu-sample-batch", type=int, default=1)
     return ap.parse_args()
 
@@ -151,10 +156,13 @@ def main():
     wl = synth.workload(args.workload)
     if args.grad_accum:
         wl = wl.replace(grad_accum=args.grad_accum)
-    cfg = g.config_for(wl, "bf16")
+    cfg = g.config_for(wl, "bf16", fused_head=int(args.fused_head), recompute=args.recompute)
+    if args.fused_head:
+        args.no_roofline = True
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()
-    log(f"bench: {wl.name} bf16, B={wl.micro_batch} T={wl.seq_len} k={wl.grad_accum}")
+    log(f"bench: {wl.name} bf16, B={wl.micro_batch} T={wl.seq_len} k={wl.grad_accum}, "
+        f"fused_head={int(args.fused_head)} recompute={args.recompute}")
 
     with torch.cuda.stream(stream):
         model = g.Model(cfg, stream=stream)
@@ -230,7 +238,8 @@ def main():
                    "n_embd": wl.n_embd, "vocab": wl.vocab_size,
                    "padded_vocab": wl.padded_vocab_size, "micro_batch": wl.micro_batch,
                    "seq_len": wl.seq_len, "grad_accum": wl.grad_accum,
-                   "tokens_per_step": wl.tokens_per_step, "parallelism": "single-gpu"},
+                   "tokens_per_step": wl.tokens_per_step, "parallelism": "single-gpu",
+                   "fused_head": int(args.fused_head), "recompute": args.recompute},
         "mfu": round(mfu, 4), "flops_per_token": fpt,
         "roofline": roof, "other_kernels": others, "cpu_baseline": cpu,
     }
