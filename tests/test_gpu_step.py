@@ -558,6 +558,8 @@ def test_gpt2_124m_full_size_sampled_sequences_match_oracle():
 
 @pytest.mark.parametrize("shape", [
     dict(B=8, n_layer=1, vocab_size=300, padded_vocab_size=320),  # one block, a ragged tile
+    dict(B=4, n_layer=1, vocab_size=4800, padded_vocab_size=4864),  # blocks of 4608 and 256
+    dict(B=4, n_layer=1, vocab_size=9300, padded_vocab_size=9344),  # 4608, then 4608 + 128
     dict(B=4, n_layer=1, n_embd=768, n_head=12, vocab_size=50257, padded_vocab_size=50304)])
 def test_fused_head_matches_oracle_and_stored_logits(shape):
     """fused_head = 1 (no logits stored; the backward regenerates their

@@ -107,8 +107,14 @@ Layout make_layout(const gpt2_config& c) {
 
 // fused_head: the backward regenerates the logit gradient this many
 // vocabulary columns at a time (24 tiles of 192 columns; 151 MB at
-// B x T = 16 x 1024)
+// B x T = 16 x 1024).  A remainder narrower than 256 columns (the least the
+// large tiles take) joins the block before it, so a block holds at most
+// kHeadChunk + 192 columns (the padded vocabulary is a multiple of 64).
 constexpr int kHeadChunk = 4608;
+int head_block_cols(int Vp, int col0) {
+  const int rest = Vp - col0;
+  return rest - kHeadChunk < 256 ? rest : kHeadChunk;
+}
 
 int validate(const gpt2_config* c) {
   if (!c) return fail(GPT2_EINVAL, "config is NULL");
@@ -137,8 +143,8 @@ int validate(const gpt2_config* c) {
     if (c->padded_vocab_size % 64 != 0)
       return fail(GPT2_EINVAL, "fused_head needs padded_vocab_size a multiple of 64");
     if (!gemm_rowstats_ok(BF16, (int)M, c->padded_vocab_size, c->n_embd, c->n_embd, c->n_embd) ||
-        !gemm_dlogits_ok(BF16, (int)M, std::min(c->padded_vocab_size, kHeadChunk), c->n_embd,
-                         c->n_embd, c->n_embd, kHeadChunk))
+        !gemm_dlogits_ok(BF16, (int)M, head_block_cols(c->padded_vocab_size, 0), c->n_embd,
+                         c->n_embd, c->n_embd, kHeadChunk + 192))
       return fail(GPT2_EINVAL, "fused_head needs micro_batch * seq_len >= 256 and padded_vocab_size >= 256");
   }
   return GPT2_OK;
@@ -296,7 +302,11 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
   md.fused_head = c.fused_head != 0;
   if (md.fused_head) {
     md.logits = md.dlogits = nullptr;
-    md.head_ld = std::min<int64_t>(c.padded_vocab_size, kHeadChunk);
+    md.head_ld = 0;  // the widest block
+    for (int col0 = 0, nc = 0; col0 < c.padded_vocab_size; col0 += nc) {
+      nc = head_block_cols(c.padded_vocab_size, col0);
+      md.head_ld = std::max<int64_t>(md.head_ld, nc);
+    }
     const int64_t ncols = gemm_rowstats_cols(c.padded_vocab_size);
     md.head_chunk = cv.take(std::max<int64_t>(M * md.head_ld * es, round_up(M * ncols * 8, 256) + M * 4));
     md.dlnf32 = (float*)cv.take(M * C * 4);
@@ -338,8 +348,8 @@ size_t plan(const gpt2_config& c, char* base, gpt2_model* mdl) {
     for (auto& sh : dWshapes) gw = std::max(gw, gemm_workspace_bytes(dt, sh[0], sh[1], Mi, EPI_ACC_F32));
     if (c.fused_head) {  // the head's gradient per block of vocabulary rows
       const int Vp = c.padded_vocab_size;
-      gw = std::max(gw, gemm_workspace_bytes(dt, std::min(Vp, kHeadChunk), Ci, Mi, EPI_ACC_F32));
-      if (Vp % kHeadChunk) gw = std::max(gw, gemm_workspace_bytes(dt, Vp % kHeadChunk, Ci, Mi, EPI_ACC_F32));
+      for (int col0 = 0; col0 < Vp; col0 += head_block_cols(Vp, col0))
+        gw = std::max(gw, gemm_workspace_bytes(dt, head_block_cols(Vp, col0), Ci, Mi, EPI_ACC_F32));
     }
     // the four weight gradients of a layer as one launch (shapes and pitches only)
     const AccItem grp[4] = {{Ci, 4 * Ci, nullptr, Ci, nullptr, 4 * Ci, nullptr, 4 * Ci},
@@ -751,8 +761,8 @@ int gpt2_backward(gpt2_model* md) {
     // d lnf += dz wte (fp32 over the blocks) and dwte += dz^T lnf
     const float seed = (float)(1.0 / ((double)md->M * md->k));
     LAUNCH(fill_f32(md->dlnf32, 0.f, (int64_t)M * C, s));
-    for (int col0 = 0; col0 < md->Vp; col0 += kHeadChunk) {
-      const int nc = std::min(kHeadChunk, md->Vp - col0);
+    for (int col0 = 0, nc = 0; col0 < md->Vp; col0 += nc) {
+      nc = head_block_cols(md->Vp, col0);
       const void* wc = (const char*)md->wt(Ly.wte) + (int64_t)col0 * C * dsize(dt);
       LAUNCH(gemm_dlogits(M, nc, C, md->lnf, C, wc, C, md->ce_lse, md->targets_keep, col0, md->V,
                           seed, md->head_chunk, md->head_ld, s));
