@@ -401,15 +401,20 @@ def test_bf16_width_768_long_token_runs_match_oracle():
     assert rel_l2(G["wte"][row], O["wte"][row]) <= 2e-2
 
 
-@pytest.mark.parametrize("dtype,shape", [("fp32", {}), ("bf16", dict(B=4, n_layer=2, n_embd=768,
-                                                                     n_head=12))])
+@pytest.mark.parametrize("dtype,shape", [
+    ("fp32", {}), ("bf16", dict(B=4, n_layer=2, n_embd=768, n_head=12)),
+    ("bf16", dict(B=4, n_layer=2, n_embd=768, n_head=12, vocab_size=300, padded_vocab_size=320,
+                  fused_head=1))])  # with the head's logits never stored
 def test_recompute_is_bit_identical(dtype, shape):
     """Recomputing the GELU output (recompute 1) and also the LayerNorm
     outputs (recompute 2) in the backward gives the same losses, gradients
     and updated parameters bit for bit as keeping them: two optimizer steps
     of two micro-steps."""
+    shape = dict(shape)
+    fused = shape.pop("fused_head", 0)
     wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", dtype, k=2, **shape)
-    print(f"{dtype} recompute 0/1/2", flush=True)
+    cfg.fused_head = fused
+    print(f"{dtype} recompute 0/1/2, fused_head {fused}", flush=True)
     res = []
     for r in range(3):
         cfg.recompute = r
