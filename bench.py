@@ -55,7 +55,8 @@ def parse():
                          "roofline entry, since the lm_head product it reports does not run")
     ap.add_argument("--recompute", type=int, default=0, choices=(0, 1, 2),
                     help="activation recompute (gpt2_config.recompute)")
-    ap.add_argument("--cpu-sample-batch", type=int, default=1)
+    ap.add_argument("--cpu-sample-batch", type=int, default=3,
+                    help="sequences in the oracle's timed sample (about 5 s of CPU work each)")
     return ap.parse_args()
 
 
@@ -144,8 +145,8 @@ def cpu_baseline(wl, B_sample):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU data "
-              "parallelism is not part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): data parallelism "
+              "over several GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
