@@ -199,6 +199,28 @@ __device__ __forceinline__ void colsum_rows128(float* __restrict__ dst, const f3
   __syncthreads();
 }
 
+// Workgroup -> (batch x head, rank), rank 0 being the head's longest causal
+// block.  Each XCD gets a contiguous range of logical workgroups
+// (xcd_remap).  Where that range is whole heads (B*H a multiple of 8), the
+// XCD runs its blocks longest-first across all of its heads, so that the
+// short blocks fill the slots the long ones leave at the end (a workgroup
+// slot then takes about the average work instead of up to one and a half
+// times it); otherwise head by head, longest first.  The blocks of a head
+// stay on one XCD and share its L2 either way.
+__device__ __forceinline__ void causal_block(int bid, int nblocks, int nper, int& bh, int& rank) {
+  const int pid = xcd_remap(bid, nblocks);
+  const int nbh = nblocks / nper;
+  if (nbh % 8 == 0) {
+    const int hx = nbh / 8;  // heads per XCD
+    const int xcd = pid / (hx * nper), p = pid % (hx * nper);
+    bh = xcd * hx + p % hx;
+    rank = p / hx;
+  } else {
+    bh = pid / nper;
+    rank = pid % nper;
+  }
+}
+
 // --------------------------------------------------------------- forward
 // Online softmax with a lazily moved reference: each query keeps a running
 // reference m (log2 units) and accumulates l = sum exp2(s c - m) and
@@ -220,11 +242,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
   const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
-  // head-major logical order, longest query block first within a head, so
-  // that the blocks of one head run on one XCD and share its L2
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = nqb - 1 - pid % nqb;
-  const int bh = pid / nqb, b = bh / H, hh = bh % H;
+  // longest query block first (causal_block)
+  int bh, rank;
+  causal_block(blockIdx.x, gridDim.x, nqb, bh, rank);
+  const int qb = nqb - 1 - rank;
+  const int b = bh / H, hh = bh % H;
   const int C = H * HD;
   const int64_t ld = 3LL * C;
   const bf16* base = qkv + (int64_t)b * T * ld;
@@ -372,11 +394,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE];  // [stage][K | V]
   const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
-  // head-major logical order, longest query block first within a head, so
-  // that the blocks of one head run on one XCD and share its L2
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = nqb - 1 - pid % nqb;
-  const int bh = pid / nqb, b = bh / H, hh = bh % H;
+  // longest query block first (causal_block)
+  int bh, rank;
+  causal_block(blockIdx.x, gridDim.x, nqb, bh, rank);
+  const int qb = nqb - 1 - rank;
+  const int b = bh / H, hh = bh % H;
   const int C = H * HD;
   const int64_t ld = 3LL * C;
   const bf16* base = qkv + (int64_t)b * T * ld;
@@ -500,11 +522,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) float LD[2][2][TB];   // [stage][L | D]
   const int lane = threadIdx.x % 64, h2 = lane / 32, l32 = lane % 32;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform per wave
-  // head-major logical order, longest key block (the first) first
+  // longest key block (the first) first (causal_block)
   const int nkb_total = (int)cdiv(T, WQ);
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  const int kblk = pid % nkb_total;
-  const int bh = pid / nkb_total, b = bh / H, hh = bh % H;
+  int bh, kblk;
+  causal_block(blockIdx.x, gridDim.x, nkb_total, bh, kblk);
+  const int b = bh / H, hh = bh % H;
   const int C = H * HD;
   const int64_t ld = 3LL * C;
   const bf16* base = qkv + (int64_t)b * T * ld;
