@@ -218,3 +218,63 @@ def test_initial_loss_close_to_ln_vocab(golden):
     closed = math.log(V) + 0.5 * 0.02 ** 2 * 768
     assert abs(loss - g["loss"]) <= 0.4
     assert abs(loss - closed) <= 0.1, (loss, closed)
+
+
+def test_train_step_matches_torch_clip_and_adamw():
+    """oracle.train_step as a whole -- k micro-steps of accumulated gradients,
+    the global-norm clip applied to the gradient before AdamW's moments, the
+    step count t advancing from 1, weight decay on 2-D tensors only ([wiki]
+    training recipe) -- against the torch autograd model above followed by
+    torch.nn.utils.clip_grad_norm_ and torch.optim.AdamW with a decayed 2-D
+    group and an undecayed 1-D group.  Two optimizer steps of two micro-steps
+    each, with a gradient norm far above the threshold so that the clip
+    scales every step (at t = 1 Adam's update is ~sign(g) whatever the
+    scale, so m and v carry the evidence; the second step needs the scales
+    of both).  The norm is ~4e4, which makes the library routine's +1e-6 in
+    the clip denominator a 2e-11 relative change."""
+    cfg = tiny_cfg(Vp=16, L=2, C=16, H=2, T=8, V=11)
+    flat, _ = make_state(cfg)
+    oracle.unflatten(cfg, flat)["lnf_w"][:] *= 1e4
+    steps = []
+    for s in range(2):
+        steps.append([tokens_for(cfg, 2, 8, seed=100 + 10 * s + i) for i in range(2)])
+    lr, clip = 1e-3, 1.0
+
+    # oracle
+    p, m, v, t = flat.copy(), np.zeros_like(flat), np.zeros_like(flat), 0
+    norms = []
+    for batches in steps:
+        out = oracle.train_step(cfg, p, m, v, t, batches, lr, grad_clip=clip)
+        t = out["t"]
+        norms.append(out["norm"])
+    assert t == 2
+    assert min(norms) > 1e4 * clip  # the clip bites on both steps
+
+    # torch: one leaf per tensor, AdamW groups by dimensionality
+    layout = oracle.param_layout(cfg)
+    leaves = [torch.tensor(flat[o:o + int(np.prod(s))].reshape(s).copy(), requires_grad=True)
+              for _, o, s in layout]
+    opt = torch.optim.AdamW([{"params": [q for q in leaves if q.dim() == 2], "weight_decay": 0.1},
+                             {"params": [q for q in leaves if q.dim() == 1], "weight_decay": 0.0}],
+                            lr=lr, betas=(0.9, 0.95), eps=1e-8)
+    for batches in steps:
+        opt.zero_grad()
+        ft = torch.cat([q.reshape(-1) for q in leaves])
+        loss = sum(torch_reference_loss(cfg, ft, x, y) for x, y in batches) / len(batches)
+        loss.backward()
+        torch.nn.utils.clip_grad_norm_(leaves, clip)
+        opt.step()
+
+    def flat_of(ts):
+        return np.concatenate([q.detach().numpy().ravel() for q in ts])
+
+    tp = flat_of(leaves)
+    tm = flat_of([opt.state[q]["exp_avg"] for q in leaves])
+    tv = flat_of([opt.state[q]["exp_avg_sq"] for q in leaves])
+    assert all(int(opt.state[q]["step"]) == 2 for q in leaves)
+    for name, o, s in layout:
+        n = int(np.prod(s))
+        sl = slice(o, o + n)
+        for mine, ref, what in ((m, tm, "m"), (v, tv, "v"), (p - flat, tp - flat, "delta p")):
+            a, b = mine[sl], ref[sl]
+            assert np.linalg.norm(a - b) <= 1e-10 * max(np.linalg.norm(b), 1e-300), (name, what)
