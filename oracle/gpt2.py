@@ -354,9 +354,11 @@ def lr_schedule(step, max_lr, warmup, total, min_ratio=0.1):
 # --------------------------------------------------------------------------
 # one optimizer step
 # --------------------------------------------------------------------------
-def accumulate_grads(cfg, flat_params, batches):
+def accumulate_grads(cfg, flat_params, batches, observe=None):
     """Sum over k micro-batches of the gradient of (mean loss)/k.
-    Returns (flat grads, list of per-micro-batch mean losses)."""
+    Returns (flat grads, list of per-micro-batch mean losses).  ``observe``,
+    if given, is called with each micro-batch's forward cache (read-only use:
+    per-position losses, logits) before its backward."""
     k = len(batches)
     P = unflatten(cfg, flat_params)
     gflat = np.zeros_like(flat_params)
@@ -364,20 +366,24 @@ def accumulate_grads(cfg, flat_params, batches):
     losses = []
     for x, y in batches:
         loss, cache = forward(cfg, P, x, y)
+        if observe is not None:
+            observe(cache)
         backward(cfg, P, cache, G, seed=1.0 / (x.size * k))
         losses.append(float(loss))
+        del cache
     return gflat, losses
 
 
 def train_step(cfg, flat_params, m, v, t, batches, lr, beta1=0.9, beta2=0.95, eps=1e-8,
-               weight_decay=0.1, grad_clip=1.0):
+               weight_decay=0.1, grad_clip=1.0, observe=None):
     """zero_grad, k x (forward + backward), global norm, clip, AdamW.
 
     Updates ``flat_params``, ``m``, ``v`` in place and returns a dict with the
     new step count, the mean loss over micro-batches, the pre-clip norm, the
-    clip scale and the (unclipped) accumulated gradient.
+    clip scale and the (unclipped) accumulated gradient.  ``observe`` as for
+    accumulate_grads.
     """
-    gflat, losses = accumulate_grads(cfg, flat_params, batches)
+    gflat, losses = accumulate_grads(cfg, flat_params, batches, observe)
     norm = global_norm(gflat)
     s = clip_scale(norm, grad_clip)
     g = gflat * flat_params.dtype.type(s)

@@ -352,14 +352,33 @@ def test_kernel_timer_counts_launches_and_leaves_results_unchanged():
     n, ms = m.read_kernel_timer()
     assert n == 5 and ms > 0.0
     assert m.read_kernel_timer() == (0, 0.0)
-    # the embedding backward adds with atomics, so only near-equality holds
-    assert rel_l2(out[0]["params"], ref[0]["params"]) < 1e-6
+    # every reduction runs in a fixed order: timed and untimed steps agree bit for bit
+    assert np.array_equal(out[0]["params"], ref[0]["params"])
     m.set_kernel_timer("lm_head_fwd", 16)
     m.forward(to_dev(batches[0][0]), to_dev(batches[0][1]), None)
     assert m.read_kernel_timer()[0] == 1
     m.set_kernel_timer("none")
     m.forward(to_dev(batches[0][0]), to_dev(batches[0][1]), None)
     assert m.read_kernel_timer() == (0, 0.0)
+
+
+def test_kernel_timer_second_stream_and_layernorm_slots():
+    """The weight-gradient pair timer (events on the library's second stream
+    for six bf16 layers: pairs 5-4, 3-2 and 1-0) and the LayerNorm timers
+    (2 L + 1 launches per forward and per backward) count every launch of a
+    two-micro-step step and leave the result bit-identical."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("small", "bf16", k=2)
+    _, ref = gpu_step(cfg, flat, batches)
+    L = wl.n_layer
+    for name, per_micro in (("wgrad_pair", L // 2), ("ln_fwd", 2 * L + 1), ("ln_bwd", 2 * L + 1)):
+        m = g.Model(cfg)
+        m.set_params(to_dev(flat))
+        m.set_kernel_timer(name, 1000)
+        _, out = gpu_step(cfg, flat, batches, model=m)
+        n, ms = m.read_kernel_timer()
+        assert n == per_micro * len(batches) and ms > 0.0, (name, n, ms)
+        assert np.array_equal(out[0]["params"], ref[0]["params"]), name
+        m.close()
 
 
 def test_gradients_bitwise_repeatable():
@@ -478,17 +497,52 @@ def test_bf16_width_1600_matches_oracle():
     assert rel_l2(gs[0]["params"], orr["params"]) <= 1e-2
 
 
+def test_bf16_350m_width_four_layers_matches_oracle():
+    """The GPT-2 350M width at its own sequence length and vocabulary
+    (bf16; C = 1024, 16 heads of 64, T = 1024, Vp = 50304; four layers, B =
+    2): the general LayerNorm kernels, the 4096-deep fc-projection product,
+    and weight gradients whose two-layer group (384 tiles of 256 x 256) does
+    not fit one round of the 256 CUs, so each layer's four products run as
+    one launch alone while the second stream stays unused."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("gpt2_350m", "bf16", k=1, B=2, n_layer=4)
+    print("bf16 gpt2_350m width: 4 layers, B=2, T=1024", flush=True)
+    _, gs = gpu_step(cfg, flat, batches)
+    orr = oracle_steps(ocfg, flat, batches)[0]
+    gr = gs[0]
+    assert abs(gr["losses"][0] - orr["losses"][0]) <= 1e-2 * orr["losses"][0]
+    G, O = per_tensor(layout, gr["grads"]), per_tensor(layout, orr["grads"])
+    worst = min(G, key=lambda n: cosine(G[n], O[n]))
+    print(f"loss {gr['losses'][0]:.5f} vs {orr['losses'][0]:.5f}, worst gradient cosine {worst} "
+          f"{cosine(G[worst], O[worst]):.6f}, params rel-L2 {rel_l2(gr['params'], orr['params']):.2e}",
+          flush=True)
+    for n in G:
+        assert cosine(G[n], O[n]) >= 0.99, (n, cosine(G[n], O[n]))
+    assert abs(gr["norm"] - orr["norm"]) <= 2e-2 * orr["norm"]
+    assert rel_l2(gr["params"], orr["params"]) <= 1e-2
+    assert cosine(gr["params"] - flat, orr["params"] - flat) > 0.9
+    assert cosine(gr["m"], orr["m"]) > 0.99
+    assert cosine(gr["v"], orr["v"]) > 0.98
+
+
 def test_gpt2_1558m_shape_micro_step():
     """One micro-step at the full GPT-2 1.5B shape (48 layers, C = 1600, 25
-    heads, T = 1024, Vp = 50304; B = 2 to keep it short): a loss near
-    ln(50257) at this initialisation, finite gradients, the evaluation
-    forward's loss, and recompute 2 reproducing the gradients bit for bit."""
+    heads, T = 1024, Vp = 50304; B = 2 to keep it short).  The forward of
+    sequence 0 against the fp32 oracle (causal attention keeps the sequences
+    independent): per-position losses element by element, |d loss| <= 2 E +
+    1e-4 with E that row's largest logit error (exact: the loss is
+    log-sum-exp minus the target logit of the stored logits), E <= 0.2 (bf16
+    activations through 48 layers), final LayerNorm rows cosine >= 0.99.
+    Then finite gradients, the evaluation forward's loss, and recompute 2
+    reproducing the gradients bit for bit."""
     wl = synth.workload("gpt2_1558m").replace(micro_batch=2, grad_accum=1)
+    ocfg = oracle.Config.from_workload(wl)
     layout = [(n, o, s) for n, o, s, _ in g.param_layout(g.config_for(wl, "bf16"))]
     flat = synth.init_params(layout, wl.n_layer, wl.vocab_size, [wl.seed_id, 2])
     stream = synth.token_stream(wl, wl.micro_batch * wl.seq_len + 1)
     x, y = synth.micro_batch(stream, 0, wl.micro_batch, wl.seq_len)
     xt, yt = to_dev(x), to_dev(y)
+    T, C, V, Vp = wl.seq_len, wl.n_embd, wl.vocab_size, wl.padded_vocab_size
+    ldl = ((Vp + 63) // 64) * 64
     print("gpt2_1558m shape, B=2", flush=True)
     grads = []
     for r in (0, 2):
@@ -497,6 +551,16 @@ def test_gpt2_1558m_shape_micro_step():
         m.zero_grad()
         loss = torch.zeros(1, device="cuda")
         m.forward(xt, yt, loss)
+        if r == 0:
+            pl = torch.empty(x.size, dtype=torch.float32, device="cuda")
+            m.debug_read("losses", pl)
+            lnf = torch.empty((x.size, C), dtype=torch.bfloat16, device="cuda")
+            m.debug_read("lnf", lnf)
+            logits = torch.empty((x.size, ldl), dtype=torch.bfloat16, device="cuda")
+            m.debug_read("logits", logits)
+            torch.cuda.synchronize()
+            pl, lnf, z0 = host(pl)[:T], host(lnf)[:T], host(logits[:T, :V])
+            del logits
         m.backward()
         grads.append(host(m.get_grads()))
         lval = float(loss)
@@ -510,18 +574,44 @@ def test_gpt2_1558m_shape_micro_step():
         assert np.isfinite(lval) and abs(lval - np.log(wl.vocab_size)) < 0.5, lval
     assert np.all(np.isfinite(grads[0])) and np.linalg.norm(grads[0]) > 0
     assert np.array_equal(grads[0], grads[1])
+    del grads
+    P = oracle.unflatten(ocfg, flat)
+    _, cache = oracle.forward(ocfg, P, x[0:1], y[0:1])
+    ol, orow = cache["losses"], cache["lnf"]
+    err = np.abs(z0 - cache["logits"][:, :V]).max(axis=1)
+    d = np.abs(pl - ol)
+    cos = (lnf * orow).sum(1) / (np.linalg.norm(lnf, axis=1) * np.linalg.norm(orow, axis=1))
+    print(f"sequence 0: loss {pl.mean():.5f} vs {ol.mean():.5f}, max |d loss| {d.max():.4f}, "
+          f"max logit error {err.max():.4f}, max |d| - 2E {(d - 2 * err).max():.5f}, "
+          f"min lnf cosine {cos.min():.5f}", flush=True)
+    assert abs(pl.mean() - ol.mean()) <= 1e-2 * ol.mean()
+    assert np.all(d <= 2 * err + 1e-4)
+    assert err.max() <= 0.2
+    assert cos.min() >= 0.99
 
 
-def test_gpt2_124m_full_size_sampled_sequences_match_oracle():
-    """The GPT-2 124M configuration at its full micro-batch (bf16, B = 16,
-    T = 1024, Vp = 50304: the launch configuration of the timed step).
-    Attention is causal within a sequence, so the oracle can follow three of
-    the sixteen sequences alone: their per-position losses and final
-    LayerNorm rows must match it to the bf16 bars (sequence-mean loss rel
-    err <= 1e-2, row cosine >= 0.99), and the per-position losses must rank
-    like the oracle's (correlation >= 0.99; at this initialisation they
-    spread by ~0.5 around ln V while bf16 moves each by a few hundredths).
-    The backward of the same micro-step must leave finite gradients."""
+@pytest.mark.timeout(900)
+def test_gpt2_124m_full_step_matches_oracle():
+    """One optimizer step of GPT-2 124M in the launch configuration of the
+    timed step (bf16, B = 16, T = 1024, Vp = 50304, on a non-default stream:
+    weight-gradient pairs on the second stream, the tied head's row-split
+    gradient, the three-set buffer rotation, the batched column reductions),
+    then clip + AdamW, against oracle.train_step in fp32 over the same
+    sixteen sequences.  The oracle takes them as sixteen one-sequence
+    micro-steps, which is the same gradient (seed 1/(B T) either way; the
+    accumulation invariant is pinned on the CPU) at a sixteenth of the host
+    memory.
+
+    Bars: loss rel err <= 1e-2; per-position losses element by element:
+    |d loss| <= 2 E + 1e-4 where E is that row's largest logit error (the
+    GPU's loss is log-sum-exp minus the target logit of its stored logits,
+    and both terms move by at most E), and E <= 0.1 (bf16 activations
+    through 12 layers and a K = 768 head product: a few units of 2^-8
+    relative on logits of magnitude ~1); per-tensor gradient cosine >= 0.99;
+    gradient norm rel err <= 2e-2; updated parameters rel-L2 <= 1e-2 (with
+    cosine diagnostics on the parameter change, m and v); argmax over the
+    unpadded vocabulary equal to the oracle's at every position whose oracle
+    top-2 margin exceeds 2 E (there the order of the top two cannot flip)."""
     wl = synth.workload("gpt2_124m").replace(grad_accum=1)
     cfg = g.config_for(wl, "bf16")
     ocfg = oracle.Config.from_workload(wl)
@@ -530,35 +620,94 @@ def test_gpt2_124m_full_size_sampled_sequences_match_oracle():
     flat = synth.perturb_affine(layout, flat, [wl.seed_id, 3])
     stream = synth.token_stream(wl, wl.micro_batch * wl.seq_len + 1)
     x, y = synth.micro_batch(stream, 0, wl.micro_batch, wl.seq_len)
-    B, T, C = wl.micro_batch, wl.seq_len, wl.n_embd
-    print("gpt2_124m full micro-batch, bf16", flush=True)
-    m = g.Model(cfg)
-    m.set_params(to_dev(flat))
-    m.zero_grad()
-    loss = torch.zeros(1, device="cuda")
-    m.forward(to_dev(x), to_dev(y), loss)
-    pl = torch.empty(B * T, dtype=torch.float32, device="cuda")
-    m.debug_read("losses", pl)
-    lnf = torch.empty((B * T, C), dtype=torch.bfloat16, device="cuda")
-    m.debug_read("lnf", lnf)
-    m.backward()
-    grads = host(m.get_grads())
-    torch.cuda.synchronize()
-    pl, lnf = host(pl), host(lnf)
-    assert np.all(np.isfinite(grads)) and np.linalg.norm(grads) > 0
+    B, T, C, V, Vp = wl.micro_batch, wl.seq_len, wl.n_embd, wl.vocab_size, wl.padded_vocab_size
+    M, ldl = B * T, ((Vp + 63) // 64) * 64
+    print("gpt2_124m full step, bf16, bench launch configuration", flush=True)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        m = g.Model(cfg, stream=st)
+        m.set_params(to_dev(flat))
+        m.zero_grad()
+        loss = torch.zeros(1, device="cuda")
+        xt, yt = to_dev(x), to_dev(y)
+        m.forward(xt, yt, loss)
+        pl = torch.empty(M, dtype=torch.float32, device="cuda")
+        m.debug_read("losses", pl)
+        am = torch.empty(M, dtype=torch.int32, device="cuda")
+        m.debug_read("argmax", am)
+        lnf = torch.empty((M, C), dtype=torch.bfloat16, device="cuda")
+        m.debug_read("lnf", lnf)
+        logits = torch.empty((M, ldl), dtype=torch.bfloat16, device="cuda")
+        m.debug_read("logits", logits)
+        m.backward()
+        grads = m.get_grads().clone()
+        norm = torch.zeros(1, device="cuda")
+        m.clip_and_adamw(LR, norm_out=norm)
+        params = m.get_params()
+        mm, vv, step = m.get_opt_state()
+    st.synchronize()
+    assert step == 1
+    pl, am, lnf = host(pl), host(am).astype(np.int64), host(lnf)
+    gg, gp, gm, gv = host(grads), host(params), host(mm), host(vv)
+    del grads, params, mm, vv
+    m.close()
+    del m
     assert abs(float(loss) - pl.mean()) <= 1e-5 * pl.mean()
-    P = oracle.unflatten(ocfg, flat.astype(np.float64))
-    for b in (0, 7, 15):
-        _, cache = oracle.forward(ocfg, P, x[b:b + 1], y[b:b + 1])
-        ol, gl = cache["losses"], pl[b * T:(b + 1) * T]
-        assert abs(gl.mean() - ol.mean()) <= 1e-2 * ol.mean(), (b, gl.mean(), ol.mean())
-        assert np.corrcoef(gl, ol)[0, 1] >= 0.99, (b, np.corrcoef(gl, ol)[0, 1])
-        gr, orow = lnf[b * T:(b + 1) * T], cache["lnf"]
-        cos = (gr * orow).sum(1) / (np.linalg.norm(gr, axis=1) * np.linalg.norm(orow, axis=1))
-        assert cos.min() >= 0.99, (b, cos.min())
-        print(f"sequence {b}: loss {gl.mean():.5f} vs {ol.mean():.5f}, "
-              f"max |d loss| {np.abs(gl - ol).max():.4f}, min lnf cosine {cos.min():.5f}",
+
+    obs = []
+
+    def observe(cache):  # one sequence at a time, in order
+        b = len(obs)
+        rows = slice(b * T, (b + 1) * T)
+        z = cache["logits"][:, :V]
+        zg = logits[rows, :V].float().cpu().numpy()
+        err = np.abs(zg - z).max(axis=1)
+        top2 = np.partition(z, -2, axis=1)[:, -2:]
+        gl, orow = lnf[rows], cache["lnf"]
+        cos = (gl * orow).sum(1) / (np.linalg.norm(gl, axis=1) * np.linalg.norm(orow, axis=1))
+        obs.append(dict(loss=cache["losses"].copy(), err=err, margin=top2[:, 1] - top2[:, 0],
+                        arg=np.argmax(z, axis=1), lnf_cos=cos))
+        print(f"oracle sequence {b}: max |d loss| "
+              f"{np.abs(pl[rows] - cache['losses']).max():.4f}, max logit error {err.max():.4f}",
               flush=True)
+
+    p = flat.copy()
+    mo, vo = np.zeros_like(p), np.zeros_like(p)
+    r = oracle.train_step(ocfg, p, mo, vo, 0, [(x[b:b + 1], y[b:b + 1]) for b in range(B)], LR,
+                          observe=observe)
+    del logits
+    torch.cuda.empty_cache()
+    ol = np.concatenate([o["loss"] for o in obs])
+    err = np.concatenate([o["err"] for o in obs])
+    margin = np.concatenate([o["margin"] for o in obs])
+    oarg = np.concatenate([o["arg"] for o in obs])
+    lnf_cos = np.concatenate([o["lnf_cos"] for o in obs])
+    d = np.abs(pl - ol)
+    clear = margin > 2 * err
+    G, O = per_tensor(layout, gg), per_tensor(layout, r["grads"])
+    cos_g = {n: cosine(G[n], O[n]) for n in G}
+    worst = min(cos_g, key=cos_g.get)
+    print(f"loss {float(loss):.6f} vs {r['loss']:.6f}; per-position max |d| {d.max():.4f} "
+          f"(mean {d.mean():.5f}), max logit error {err.max():.4f}, max |d| - 2E "
+          f"{(d - 2 * err).max():.5f}; lnf cosine min {lnf_cos.min():.5f}; argmax clear "
+          f"{clear.mean():.3f}, agree {np.mean(am[clear] == oarg[clear]):.4f}; norm "
+          f"{float(norm):.5f} vs {r['norm']:.5f}; worst grad cosine {worst} {cos_g[worst]:.6f}; "
+          f"params rel-L2 {rel_l2(gp, p):.2e}; cosines dp {cosine(gp - flat, p - flat):.4f} "
+          f"m {cosine(gm, mo):.5f} v {cosine(gv, vo):.5f}", flush=True)
+    assert abs(float(loss) - r["loss"]) <= 1e-2 * r["loss"]
+    assert np.all(d <= 2 * err + 1e-4), (d - 2 * err).max()
+    assert err.max() <= 0.1
+    assert lnf_cos.min() >= 0.99
+    for n in G:
+        assert cos_g[n] >= 0.99, (n, cos_g[n])
+    assert np.all(G["wte"].reshape(Vp, C)[V:] == 0)
+    assert abs(float(norm) - r["norm"]) <= 2e-2 * r["norm"]
+    assert rel_l2(gp, p) <= 1e-2
+    assert cosine(gp - flat, p - flat) > 0.9
+    assert cosine(gm, mo) > 0.99
+    assert cosine(gv, vo) > 0.98
+    assert clear.mean() > 0.5
+    assert np.array_equal(am[clear], oarg[clear])
 
 
 @pytest.mark.parametrize("shape", [
