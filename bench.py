@@ -27,13 +27,15 @@ METRIC = "train tokens/sec + MFU, GPT-2 124M bf16 B×T=16×1024, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of one lm_head forward GEMM launch from two rocprofv3 --pmc runs
-# (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, mean of six), scaled by what the same
-# counters read for a plain 1 GiB device copy (FETCH_SIZE reads half the
-# bytes copied: factor 2.0; WRITE_SIZE is exact: factor 1.0).  Valid only for
-# the GEMM source it was measured on (first 16 hex digits of its sha256).
-LM_HEAD_TRAFFIC = {"gemm_source_sha256_16": "361b88f5cfbbed5c", "fetch_kib": 921361, "write_kib": 1609728,
-                   "fetch_factor": 2.0, "write_factor": 1.0}
+# HBM traffic of one launch of the dominant kernel (the weight gradients of
+# two layers, gemm_big_kernel<256,256,false,false,EPI_ACC_F32>, 216 tiles)
+# from two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, mean over the timed pairs), each scaled by
+# what the same counter reads for a plain device copy of known size.  Valid
+# only for the GEMM source it was measured on (first 16 hex digits of its
+# sha256); None until measured.  Source: profiles/gpt2_124m_bf16_train_step_counters.md.
+WGRAD_TRAFFIC = {"gemm_source_sha256_16": "361b88f5cfbbed5c", "shape": [16384, 768], "fetch_kib": 519310.0,
+                 "write_kib": 55296.0, "fetch_factor": 2.0, "write_factor": 1.0}
 
 
 def log(*a):
@@ -51,50 +53,78 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--fused-head", action="store_true",
-                    help="train without stored logits (gpt2_config.fused_head = 1); no "
-                         "roofline entry, since the lm_head product it reports does not run")
+                    help="train without stored logits (gpt2_config.fused_head = 1)")
     ap.add_argument("--recompute", type=int, default=0, choices=(0, 1, 2),
                     help="activation recompute (gpt2_config.recompute)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run three plain device-to-device copies of this many MiB "
+                         "(the reference dispatches for scaling hardware traffic counters)")
     ap.add_argument("--cpu-sample-batch", type=int, default=3,
                     help="sequences in the oracle's timed sample (about 5 s of CPU work each)")
     return ap.parse_args()
 
 
-def lm_head_roofline(cfg, n, total_ms):
-    """bf16 lm_head forward GEMM (M = B*T, N = Vp, K = C): the largest single
-    launch of the step, one per micro-step.  Algorithmic flops per launch
-    2 M N K; duration from the library's event pairs around each launch of it
-    inside the timed steps."""
+def wgrad_pair_flops(cfg):
+    """Algorithmic flops of one launch of two layers' weight gradients:
+    dW += dy^T x for fc-proj (C x 4C), fc (4C x C), proj (C x C) and qkv
+    (3C x C) of each layer, K = B*T tokens: 2 * 2 * B*T * 12 C^2."""
+    C, M = cfg.n_embd, cfg.micro_batch * cfg.seq_len
+    return 2.0 * 2 * M * 12 * C * C
+
+
+def wgrad_pair_roofline(cfg, n, total_ms):
+    """Roofline entry for the dominant kernel of the step: the grouped launch
+    of two layers' weight gradients (eight products, one 256 x 256 tile per
+    workgroup, fp32 accumulation into the gradients), which runs on the
+    library's second stream beside the next layer's input-gradient work.
+    Duration from the library's event pairs around each such launch inside
+    the timed steps."""
     import hashlib
-    M, N, K = cfg.micro_batch * cfg.seq_len, cfg.padded_vocab_size, cfg.n_embd
-    t = total_ms / 1e3 / n
-    achieved = 2.0 * M * N * K / t / 1e12
+    C, M = cfg.n_embd, cfg.micro_batch * cfg.seq_len
+    t = total_ms / 1e3 / max(n, 1)
+    flops = wgrad_pair_flops(cfg)
+    achieved = flops / t / 1e12
+    # per layer: the bf16 operands dy and x of the four products, read once
+    # (columns C + 4C, 4C + C, C + C, 3C + C: 16 C per token), and the 12 C^2
+    # fp32 gradients, read and written
+    alg = 2 * (2 * M * 16 * C + 8 * 12 * C * C)
     traffic = None
     src = os.path.join(ROOT, "transformer_lm_pretraining_train_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    tr = LM_HEAD_TRAFFIC
-    if sha == tr["gemm_source_sha256_16"] and (M, N, K) == (16384, 50304, 768):
-        traffic = int(tr["fetch_kib"] * 1024 * tr["fetch_factor"] + tr["write_kib"] * 1024 * tr["write_factor"])
-    return {"kernel": "gemm_big_kernel<256,256,true,true,EPI_STORE> (lm_head forward, "
-                      f"M={M} N={N} K={K})",
+    tr = WGRAD_TRAFFIC
+    if tr and sha == tr["gemm_source_sha256_16"] and (M, C) == tuple(tr["shape"]):
+        traffic = int(tr["fetch_kib"] * 1024 * tr["fetch_factor"]
+                      + tr["write_kib"] * 1024 * tr["write_factor"])
+    return {"kernel": "gemm_big_kernel<256,256,false,false,EPI_ACC_F32> (weight gradients of two "
+                      f"layers: 8 products, K={M}, {2 * 12 * C * C} outputs)",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "traffic_unit": "bytes per launch", "algorithmic_bytes": 2 * (M * K + N * K + M * N),
-            "avg_launch_us": round(t * 1e6, 1), "launches_timed": n}
+            "traffic_unit": "bytes per launch", "algorithmic_bytes": alg,
+            "flops_per_launch": flops, "avg_launch_us": round(t * 1e6, 1), "launches_timed": n}
 
 
 def other_kernels(cfg, n_timed):
-    """Algorithmic work per launch of the other timed steps: causal attention
-    (4 hd flops per query-key pair forward, 10 hd backward), the fused
-    cross-entropy of the forward (one bf16 read of each logit row and one bf16
-    write of its gradient) and AdamW (30 bytes per parameter: read p, g, m, v,
-    write p, m, v and the bf16 copy)."""
+    """Algorithmic work per launch of the other main kernels, each timed over
+    one extra step: the lm_head forward product (2 M Vp C flops), causal
+    attention (4 hd flops per query-key pair forward, 10 hd backward), the
+    fused cross-entropy of the forward (one bf16 read of each logit row and
+    one bf16 write of its gradient) and AdamW (30 bytes per parameter: read
+    p, g, m, v, write p, m, v and the bf16 copy).  The LayerNorm entries
+    (forward: bf16 row in and out, fp32 mean and rstd out; backward: bf16 dy,
+    x and the incoming residual gradient in, bf16 dx out, fp32 mean and rstd
+    in, none incoming for the final LayerNorm) are computed here but not
+    timed by main(): an event pair adds several microseconds to a 10-25 us
+    launch, so their rates come from the profiler's kernel trace."""
     import transformer_lm_pretraining_train_amd as g
-    B, T, H, C = cfg.micro_batch, cfg.seq_len, cfg.n_head, cfg.n_embd
+    B, T, H, C, L = cfg.micro_batch, cfg.seq_len, cfg.n_head, cfg.n_embd, cfg.n_layer
+    M = B * T
     hd = C // H
     pairs = B * H * T * (T + 1) // 2
-    work = {"attn_fwd": (4.0 * hd * pairs, "mfma"), "attn_bwd": (10.0 * hd * pairs, "mfma"),
-            "ce_fwd": (4.0 * B * T * cfg.padded_vocab_size, "hbm"),
+    ln_bwd = (2 * L * (8 * C + 8) + (6 * C + 8)) * M / (2 * L + 1)
+    work = {"lm_head_fwd": (2.0 * M * cfg.padded_vocab_size * C, "mfma"),
+            "attn_fwd": (4.0 * hd * pairs, "mfma"), "attn_bwd": (10.0 * hd * pairs, "mfma"),
+            "ce_fwd": (4.0 * M * cfg.padded_vocab_size, "hbm"),
+            "ln_fwd": ((4.0 * C + 8) * M, "hbm"), "ln_bwd": (ln_bwd, "hbm"),
             "adamw": (30.0 * g.num_params(cfg), "hbm")}
     out = {}
     for name, (n, ms) in n_timed.items():
@@ -109,8 +139,31 @@ def other_kernels(cfg, n_timed):
             a = w / t / 1e9
             out[name] = {"bound": bound, "achieved": round(a, 1), "unit": "GB/s",
                          "peak": PEAK_HBM_GBS, "frac": round(a / PEAK_HBM_GBS, 4),
-                         "avg_launch_us": round(t * 1e6, 1), "launches_timed": n}
+                         "bytes_per_launch": int(w), "avg_launch_us": round(t * 1e6, 1),
+                         "launches_timed": n}
     return out
+
+
+def host_info():
+    """CPU model (/proc/cpuinfo) and the BLAS library NumPy runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return model, blas
 
 
 def cpu_baseline(wl, B_sample):
@@ -121,7 +174,8 @@ def cpu_baseline(wl, B_sample):
     import synth
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
     except Exception:
         threads = os.cpu_count() or 1
     ocfg = oracle.Config.from_workload(wl)
@@ -135,8 +189,9 @@ def cpu_baseline(wl, B_sample):
     oracle.train_step(ocfg, flat, m, v, 0, [(x, y)], 6e-4)
     dt = time.perf_counter() - t0
     toks = B_sample * wl.seq_len
+    cpu_model, blas = host_info()
     return {"value": round(toks / dt, 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
             "sample": f"{wl.name}: one micro-step of B={B_sample} x T={wl.seq_len} tokens "
                       f"(fwd + bwd) plus one clip + AdamW over all parameters, fp32 NumPy; "
                       f"{dt:.1f} s"}
@@ -158,9 +213,16 @@ def main():
     if args.grad_accum:
         wl = wl.replace(grad_accum=args.grad_accum)
     cfg = g.config_for(wl, "bf16", fused_head=int(args.fused_head), recompute=args.recompute)
-    if args.fused_head:
-        args.no_roofline = True
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: three device copies of {n} bytes")
+        del src, dst
     stream = torch.cuda.Stream()
     log(f"bench: {wl.name} bf16, B={wl.micro_batch} T={wl.seq_len} k={wl.grad_accum}, "
         f"fused_head={int(args.fused_head)} recompute={args.recompute}")
@@ -193,7 +255,7 @@ def main():
             log(f"warmup step {s + 1}: loss {losses.mean().item():.4f} norm {norm.item():.4f}")
         stream.synchronize()
         if not args.no_roofline:
-            model.set_kernel_timer("lm_head_fwd", args.steps * wl.grad_accum)
+            model.set_kernel_timer("wgrad_pair", args.steps * wl.grad_accum * (wl.n_layer // 2 + 1))
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -213,12 +275,15 @@ def main():
 
     roof = others = None
     if not args.no_roofline:
-        roof = lm_head_roofline(cfg, *model.read_kernel_timer())
+        roof = wgrad_pair_roofline(cfg, *model.read_kernel_timer())
         log(f"roofline: {roof}")
         # one more step per timed kernel, outside the timed region
         timed = {}
+        names = ["attn_fwd", "attn_bwd", "adamw"]
+        if not args.fused_head:
+            names += ["lm_head_fwd", "ce_fwd"]
         with torch.cuda.stream(stream):
-            for s, name in enumerate(("attn_fwd", "attn_bwd", "ce_fwd", "adamw")):
+            for s, name in enumerate(names):
                 model.set_kernel_timer(name, 4096)
                 step(args.warmup + args.steps + s + 1)
                 timed[name] = model.read_kernel_timer()

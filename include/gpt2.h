@@ -147,9 +147,13 @@ int gpt2_set_grads(gpt2_model* model, const float* dev_src);
 int gpt2_get_opt_state(gpt2_model* model, float* dev_m, float* dev_v, int64_t* step);
 int gpt2_set_opt_state(gpt2_model* model, const float* dev_m, const float* dev_v, int64_t step);
 
-/* Forward pass on dev_tokens (B, T).  With dev_targets (B, T) non-NULL it
- * also evaluates the cross-entropy and writes the mean over the B*T
- * positions (not divided by k) to dev_loss (one float; may be NULL).
+/* Forward pass on dev_tokens (B, T): embeddings, the pre-LayerNorm blocks,
+ * the final LayerNorm and the tied head over the padded vocabulary (qntz.me
+ * "From 0 to 1 build GPT", building the Transformer; "Let's reproduce GPT-2
+ * (124M)" notes, training recipe: weight tying; GPU optimisation ladder:
+ * vocabulary 50257 -> 50304).  With dev_targets (B, T) non-NULL it also
+ * evaluates the cross-entropy and writes the mean over the B*T positions
+ * (not divided by k) to dev_loss (one float; may be NULL).
  * Out-of-range ids are clamped for memory safety and reported as
  * GPT2_ETOKEN by the next gpt2_sync / gpt2_clip_and_adamw. */
 int gpt2_forward(gpt2_model* model, const int32_t* dev_tokens, const int32_t* dev_targets,
@@ -170,7 +174,10 @@ int gpt2_forward_loss(gpt2_model* model, const int32_t* dev_tokens, const int32_
                       float* dev_loss);
 
 /* Backward pass of the last forward (which must have had targets):
- * gradients += d(mean loss / k) / d params.  The logit gradient comes from
+ * gradients += d(mean loss / k) / d params, the micro-step's share under
+ * gradient accumulation ("Let's reproduce GPT-2 (124M)" notes, training
+ * recipe: the loss is divided by the number of accumulation steps; the tied
+ * wte gets both its head and its embedding gradient).  The logit gradient comes from
  * the forward's cross-entropy (computed with the loss, from the same read of
  * the logits); the logits themselves are left as the forward wrote them.
  * With fused_head = 1 it is regenerated here instead (see gpt2_config).
@@ -178,7 +185,9 @@ int gpt2_forward_loss(gpt2_model* model, const int32_t* dev_tokens, const int32_
  * its targets are kept by the model. */
 int gpt2_backward(gpt2_model* model);
 
-/* Gradients = 0. */
+/* Gradients = 0: the start of an optimizer step's k accumulated micro-steps
+ * ("Let's reproduce GPT-2 (124M)" notes, training recipe: gradient
+ * accumulation). */
 int gpt2_zero_grad(gpt2_model* model);
 
 /* One optimizer step ("Let's reproduce GPT-2 (124M)", training recipe):
@@ -199,7 +208,7 @@ int gpt2_sync(gpt2_model* model);
  * norm at every step (setup section), flags that save a checkpoint every n
  * steps and resume a crashed run with bit-identical results (flags
  * section), and a restart that skips an update whose loss or norm z-score
- * exceeds 5 (results section).  These calls provide those pieces. */
+ * exceeds 5 (400B-token run section).  These calls provide those pieces. */
 
 /* Rolling z-score detector over the last `window` finite values of a
  * series, 2 <= window <= 65536 (host only, no GPU calls).
@@ -211,6 +220,17 @@ typedef struct gpt2_zscore gpt2_zscore;
 int gpt2_zscore_create(int window, gpt2_zscore** out);
 int gpt2_zscore_update(gpt2_zscore* detector, double x, double* z_out);
 int gpt2_zscore_destroy(gpt2_zscore* detector);
+
+/* A detector's state, for checkpoints of a guarded run: the values it
+ * holds, oldest first.  gpt2_zscore_get_state writes the window size and
+ * the number of values held (either pointer may be NULL) and, if `values`
+ * is non-NULL, the values (cap must be >= that number).
+ * gpt2_zscore_set_state replaces the held values with `count` values,
+ * oldest first (0 <= count <= window, all finite); updates then continue
+ * exactly as in the detector the values came from.  EINVAL otherwise. */
+int gpt2_zscore_get_state(const gpt2_zscore* detector, double* values, int cap, int* window,
+                          int* count);
+int gpt2_zscore_set_state(gpt2_zscore* detector, const double* values, int count);
 
 /* The optimizer step of gpt2_clip_and_adamw in two calls.  gpt2_grad_norm
  * computes the global L2 norm of the gradients and the clip scale
@@ -252,8 +272,11 @@ int gpt2_skip_counts(gpt2_model* model, int64_t* nonfinite, int64_t* outlier);
  * padded_vocab_size; the dtype and batch shape may differ), refreshes the
  * bf16 parameter copy and zeroes the gradients.  A run resumed from a
  * checkpoint taken between optimizer steps, fed the same micro-batches,
- * reproduces the uninterrupted run bit for bit: no other state carries
- * from one step to the next.  EINVAL: the file cannot be opened, read or
+ * reproduces the uninterrupted run bit for bit: the file holds all the
+ * model's state that carries from one step to the next.  The z-score
+ * detectors of gpt2_guarded_step are the caller's host objects and are not
+ * in the file: a guarded run resumes bit for bit when their windows are
+ * saved and restored beside it (gpt2_zscore_get_state / set_state).  EINVAL: the file cannot be opened, read or
  * written, is short, has another magic or version, or another shape.  Both
  * wait for the stream. */
 int gpt2_save_state(gpt2_model* model, const char* path);
@@ -291,18 +314,26 @@ int gpt2_debug_read(gpt2_model* model, int which, int layer, void* dev_dst, size
  *   ATTN_BWD     attention backward (both of its kernels), one pair per layer
  *   CE_FWD       the fused softmax cross-entropy of each forward with targets
  *                (loss, lse, argmax and the logit gradient)
- *   ADAMW        the AdamW update of each optimizer step (not the norm) */
+ *   ADAMW        the AdamW update of each optimizer step (not the norm)
+ *   WGRAD_PAIR   each launch of the weight gradients of two layers (eight
+ *                products, bf16), on the stream it runs on (the library's
+ *                second stream when it has one)
+ *   LN_FWD       every LayerNorm forward of the forward pass
+ *   LN_BWD       every LayerNorm backward of the backward pass */
 enum {
   GPT2_TIMER_NONE = 0,
   GPT2_TIMER_LM_HEAD_FWD = 1,
   GPT2_TIMER_ATTN_FWD = 2,
   GPT2_TIMER_ATTN_BWD = 3,
   GPT2_TIMER_CE_FWD = 4,
-  GPT2_TIMER_ADAMW = 5
+  GPT2_TIMER_ADAMW = 5,
+  GPT2_TIMER_WGRAD_PAIR = 6,
+  GPT2_TIMER_LN_FWD = 7,
+  GPT2_TIMER_LN_BWD = 8
 };
 int gpt2_set_kernel_timer(gpt2_model* model, int which, int max_launches);
 
-/* Waits for the stream, then reports how many launches were timed since the
+/* Waits for the streams, then reports how many launches were timed since the
  * timer was set or last read (*launches) and the sum of their event-pair
  * durations in milliseconds (*total_ms), and restarts the count. */
 int gpt2_read_kernel_timer(gpt2_model* model, int* launches, double* total_ms);

@@ -33,8 +33,10 @@ enum {
 /* C(m, n) = sum_{k < K} A(m, k) B(n, k) for m < M, n < N, then the epilogue,
  * with fp32 accumulation.  The linear layers of the model are this product
  * with W stored (out, in): y = x W^T (A, B k-major), dx = dy W (A k-major,
- * B n-major), dW += dy^T x (A m-major, B n-major) ("Let's reproduce GPT-2
- * (124M)" notes: the model is built from such matrix multiplies).
+ * B n-major), dW += dy^T x (A m-major, B n-major).  The linear layers are
+ * the qkv, output-projection and MLP products of each block (qntz.me "From 0
+ * to 1 build GPT", building the Transformer) and the tied head; their
+ * gradients follow from differentiating y = x W^T + b.
  *   a_kmajor != 0: A(m, k) = A[m*lda + k], else A[k*lda + m];
  *   b_kmajor != 0: B(n, k) = B[n*ldb + k], else B[k*ldb + n].
  * Leading dimensions (elements) must be multiples of 8, and each row of A
@@ -52,9 +54,9 @@ int gpt2k_gemm(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K, const
                size_t ws_bytes, void* hip_stream);
 
 /* gpt2k_gemm that also writes per-block column sums of its output, the
- * first stage of a bias gradient (the bias of a linear layer gets the sum of
- * the output gradient over all token rows; "Let's reproduce GPT-2 (124M)",
- * the backward pass of a linear layer):
+ * first stage of a bias gradient (for y = x W^T + b, the gradient of b is
+ * the sum of the output gradient over all token rows; the linear layers
+ * are those of qntz.me "From 0 to 1 build GPT", building the Transformer):
  *   colsum[b*ldcs + n] = sum over the rows m in [64b, 64b + 64) ∩ [0, M) of
  *   the stored out(m, n), as rounded to `dtype`, for b < ceil(M / 64), n < N,
  * each sum in a fixed order (deterministic).  dev_colsum (fp32, 8-byte
@@ -74,8 +76,8 @@ int gpt2k_gemm_colsum(int dtype, int a_kmajor, int b_kmajor, int M, int N, int K
 /* Weight gradients of up to eight linear layers over the same K tokens:
  * out_i(m, n) += sum_{k < K} A_i[k*lda_i + m] B_i[k*ldb_i + n] for
  * m < M_i, n < N_i, i < n, 1 <= n <= 8 (dW += dy^T x with dy, x stored
- * row-major; "Let's reproduce GPT-2 (124M)": the backward pass of each
- * linear layer).  M, N, lda, ldb, ldo are host arrays of n entries; dev_A,
+ * row-major: the weight gradient of y = x W^T + b for each linear layer of a
+ * block, qntz.me "From 0 to 1 build GPT", building the Transformer).  M, N, lda, ldb, ldo are host arrays of n entries; dev_A,
  * dev_B, dev_out host arrays of n device pointers; out_i is fp32, A_i and
  * B_i are of `dtype`.  In bf16 the products run as one launch whose K is
  * split in a fixed order when gpt2k_gemm_acc_group_workspace_bytes() of
@@ -107,9 +109,9 @@ int gpt2k_attention_backward(int dtype, void* dev_dqkv, const void* dev_dout, co
                              int hd, void* dev_scratch, void* hip_stream);
 
 /* gpt2k_attention_backward that also writes per-block column sums of dqkv,
- * the first stage of the qkv bias gradient (sum of d qkv over all token
- * rows; "Let's reproduce GPT-2 (124M)", the backward pass of the qkv linear
- * layer):
+ * the first stage of the qkv bias gradient (the sum of d qkv over all
+ * token rows, the bias gradient of the qkv linear layer of qntz.me "From 0
+ * to 1 build GPT", building the Transformer):
  *   dev_colsum[(b*ceil(T/128) + i)*3C + c] = sum over t in
  *   [128i, 128i + 128) ∩ [0, T) of the stored dqkv(b*T + t, c)
  * (as rounded to `dtype`; fp32 sums in a fixed order), for every b < B,

@@ -21,20 +21,36 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_lm_head_roofline_arithmetic():
+def test_wgrad_pair_roofline_arithmetic():
+    """Two GPT-2 124M layers' weight gradients: 2 x 2 x 16384 x 12 x 768^2
+    = 463.9 GFLOP per launch; bytes: the bf16 operands (16 C columns per
+    token per layer) and the fp32 gradients read and written."""
     cfg = g.config_for(synth.workload("gpt2_124m"))
-    r = bench.lm_head_roofline(cfg, 4, 4 * 1.5)  # four launches of 1.5 ms
-    M, N, K = 16384, 50304, 768
-    assert r["achieved"] == pytest.approx(2 * M * N * K / 1.5e-3 / 1e12, rel=1e-4)
+    r = bench.wgrad_pair_roofline(cfg, 4, 4 * 0.5)  # four launches of 0.5 ms
+    M, C = 16384, 768
+    flops = 2 * 2 * M * 12 * C * C
+    assert r["flops_per_launch"] == flops and abs(flops - 463.9e9) < 0.1e9
+    assert r["achieved"] == pytest.approx(flops / 0.5e-3 / 1e12, rel=1e-4)
     assert r["peak"] == 2516.6 and r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
-    assert r["avg_launch_us"] == 1500.0 and r["launches_timed"] == 4
-    assert r["algorithmic_bytes"] == 2 * (M * K + N * K + M * N)
+    assert r["avg_launch_us"] == 500.0 and r["launches_timed"] == 4
+    assert r["algorithmic_bytes"] == 2 * (2 * M * 16 * C + 8 * 12 * C * C)
     if r["traffic"] is not None:  # counters taken on this GEMM source
-        assert r["traffic"] > r["algorithmic_bytes"]
+        assert r["traffic"] > 0
+
+
+def test_other_kernels_arithmetic():
+    cfg = g.config_for(synth.workload("gpt2_124m"))
+    o = bench.other_kernels(cfg, {"ln_fwd": (25, 25 * 0.010), "lm_head_fwd": (1, 1.2)})
+    M, C = 16384, 768
+    assert o["ln_fwd"]["bytes_per_launch"] == (4 * C + 8) * M
+    assert o["ln_fwd"]["achieved"] == pytest.approx((4 * C + 8) * M / 10e-6 / 1e9, rel=1e-4)
+    assert o["lm_head_fwd"]["achieved"] == pytest.approx(2 * M * 50304 * C / 1.2e-3 / 1e12,
+                                                         rel=1e-4)
 
 
 def test_cpu_baseline_reports_the_oracle():
     c = bench.cpu_baseline(synth.workload("tiny"), 1)
     assert c["kind"] == "oracle" and c["unit"] == "tokens/s"
     assert c["value"] > 0 and c["cores"] >= 1 and c["sample"].startswith("tiny:")
+    assert "cpu_model" in c and "blas" in c

@@ -1,7 +1,7 @@
 """The training-loop robustness calls on the GPU: the optimizer step split
 into gpt2_grad_norm + gpt2_adamw_update (bit-identical to
 gpt2_clip_and_adamw), the guarded step that skips an update whose gradient
-norm spikes (llm.c GPT-2 1.5B post, dszhyy.com, results section: skip on a
+norm spikes (llm.c GPT-2 1.5B post, dszhyy.com, 400B-token run section: skip on a
 loss or norm z-score above 5), and checkpoint / resume reproducing the
 uninterrupted run bit for bit (same post, flags section)."""
 import numpy as np
@@ -130,6 +130,47 @@ def test_resume_from_checkpoint_is_bitwise(dtype, tmp_path):
     assert sa[3] == sb[3] == 4
     for x, y in zip(sa[:3], sb[:3]):
         assert np.array_equal(x, y)
+
+
+def test_guarded_run_resumes_bitwise_with_its_detector_windows(tmp_path):
+    """A guarded run (gpt2_guarded_step with loss and norm detectors whose
+    windows are full) checkpointed between steps, the detectors' windows
+    saved beside the file, resumes on a fresh model and fresh detectors and
+    matches the uninterrupted run bit for bit: parameters, m, v, step, skip
+    counts and every z-score."""
+    cfg, flat, dev, k = case("bf16")
+    win = 3
+
+    def run(m, lz, nz, steps):
+        out = []
+        for step in steps:
+            grads_of(m, dev, step, k)
+            r = m.guarded_step(10.0 + 0.01 * step, LR, loss_z=lz, norm_z=nz)
+            out.append((r["z_loss"], r["z_norm"], r["skipped"]))
+        return out
+
+    a = new_model(cfg, flat)
+    la, na = g.ZScore(win), g.ZScore(win)
+    run(a, la, na, range(3))  # windows full
+    path = tmp_path / "guarded.ckpt"
+    a.save_state(str(path))
+    saved = (la.get_state(), na.get_state())
+    assert len(saved[0]) == win and len(saved[1]) == win
+    za = run(a, la, na, range(3, 6))
+    b = g.Model(cfg)
+    b.load_state(str(path))
+    lb, nb = g.ZScore(win), g.ZScore(win)
+    lb.set_state(saved[0])
+    nb.set_state(saved[1])
+    zb = run(b, lb, nb, range(3, 6))
+    for x, y in zip(za, zb):
+        assert np.array_equal(np.array(x, dtype=np.float64), np.array(y, dtype=np.float64))
+    assert all(np.isfinite(z[1]) for z in za)  # the norm windows were full: real z-scores
+    sa, sb = state(a), state(b)
+    assert sa[3] == sb[3]
+    for x, y in zip(sa[:3], sb[:3]):
+        assert np.array_equal(x, y)
+    assert a.skip_counts() == b.skip_counts()
 
 
 def test_checkpoint_rejects_other_shapes_and_bad_files(tmp_path):

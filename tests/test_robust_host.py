@@ -57,3 +57,28 @@ def test_zscore_spike_against_a_noisy_history():
 def test_zscore_window_bounds(window):
     with pytest.raises(g.GPT2Error):
         g.ZScore(window)
+
+
+def test_zscore_state_round_trip_continues_bit_for_bit():
+    """A detector rebuilt from another's state (get_state / set_state, the
+    values held, oldest first) scores every later value with the same bits,
+    before and after the window has wrapped; bad states are refused."""
+    rng = np.random.default_rng(3)
+    xs = list(rng.standard_normal(40) * 0.1 + 3.0)
+    for cut in (3, 5, 17):  # part-full, just full, wrapped
+        a = g.ZScore(5)
+        for x in xs[:cut]:
+            a.update(x)
+        st = a.get_state()
+        assert st == xs[max(0, cut - 5):cut]
+        b = g.ZScore(5)
+        b.set_state(st)
+        assert b.get_state() == st
+        for x in xs[cut:]:
+            za, zb = a.update(x), b.update(x)
+            assert (math.isnan(za) and math.isnan(zb)) or za == zb
+    c = g.ZScore(4)
+    for bad in ([1.0] * 5, [1.0, float("nan")]):
+        with pytest.raises(g.GPT2Error) as ei:
+            c.set_state(bad)
+        assert ei.value.name == "EINVAL"

@@ -32,7 +32,8 @@ ERRORS = {0: "OK", -1: "EINVAL", -2: "EWORKSPACE", -3: "ESTATE", -4: "ETOKEN",
 EPI = {"store": 0, "bias": 1, "bias_resid": 2, "bias_gelu": 3, "gelu_bwd": 4, "acc_f32": 5}
 DBG = {"logits": 0, "losses": 1, "argmax": 2, "ln1": 3, "qkv": 4, "atty": 5, "res2": 6,
        "fch": 7, "res3": 8, "lnf": 9, "att_lse": 10, "encoded": 11}
-TIMER = {"none": 0, "lm_head_fwd": 1, "attn_fwd": 2, "attn_bwd": 3, "ce_fwd": 4, "adamw": 5}
+TIMER = {"none": 0, "lm_head_fwd": 1, "attn_fwd": 2, "attn_bwd": 3, "ce_fwd": 4, "adamw": 5,
+         "wgrad_pair": 6, "ln_fwd": 7, "ln_bwd": 8}
 
 
 class GPT2Config(ctypes.Structure):
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
             "gpt2_zscore_create": (I, [I, ctypes.POINTER(P)]),
             "gpt2_zscore_update": (I, [P, D, ctypes.POINTER(D)]),
             "gpt2_zscore_destroy": (I, [P]),
+            "gpt2_zscore_get_state": (I, [P, P, I, ctypes.POINTER(I), ctypes.POINTER(I)]),
+            "gpt2_zscore_set_state": (I, [P, P, I]),
             "gpt2_grad_norm": (I, [P, F, ctypes.POINTER(F)]),
             "gpt2_adamw_update": (I, [P, F, F, F, F, F]),
             "gpt2_guarded_step": (I, [P, P, P, F, F, F, F, F, F, F, F, F, ctypes.POINTER(F),
@@ -334,6 +337,18 @@ class ZScore:
         z = ctypes.c_double()
         _check(lib().gpt2_zscore_update(self.h, float(x), ctypes.byref(z)))
         return z.value
+
+    def get_state(self):
+        """The values held, oldest first (a list of floats)."""
+        w, n = ctypes.c_int(), ctypes.c_int()
+        _check(lib().gpt2_zscore_get_state(self.h, None, 0, ctypes.byref(w), ctypes.byref(n)))
+        buf = (ctypes.c_double * max(n.value, 1))()
+        _check(lib().gpt2_zscore_get_state(self.h, buf, n.value, None, None))
+        return list(buf[:n.value])
+
+    def set_state(self, values):
+        buf = (ctypes.c_double * max(len(values), 1))(*values)
+        _check(lib().gpt2_zscore_set_state(self.h, buf, len(values)))
 
     def close(self):
         if getattr(self, "h", None):

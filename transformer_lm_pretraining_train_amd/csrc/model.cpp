@@ -389,6 +389,18 @@ int check_launch(hipError_t e, const char* what) {
     }                                                                               \
   } while (0)
 
+// The same on a given stream (the side stream's weight-gradient pairs).
+#define TIMED_ON(which, strm, expr)                                                 \
+  do {                                                                              \
+    const bool on_ = md->timer_which == (which) && md->timer_used < md->timer_cap;  \
+    if (on_) HIP_TRY(hipEventRecord(md->timer_ev[2 * md->timer_used], (strm)));     \
+    LAUNCH(expr);                                                                   \
+    if (on_) {                                                                      \
+      HIP_TRY(hipEventRecord(md->timer_ev[2 * md->timer_used + 1], (strm)));        \
+      ++md->timer_used;                                                             \
+    }                                                                               \
+  } while (0)
+
 void release_side(gpt2_model* md) {
   if (md->side) (void)hipStreamSynchronize(md->side);
   for (hipEvent_t e : md->ev_ready)
@@ -619,8 +631,8 @@ static int forward_trunk(gpt2_model* md, const int32_t* tokens, const int32_t* t
     void* ln1 = a.ln1 ? a.ln1 : md->ln_tmp;  // recompute 2: not kept
     void* ln2 = a.ln2 ? a.ln2 : md->ln_tmp;
     void* fchg = a.fchg ? a.fchg : md->fchg_tmp;  // recompute >= 1: not kept
-    LAUNCH(layernorm_forward(dt, ln1, a.ln1_mean, a.ln1_rstd, x, P + o.ln1_w, P + o.ln1_b, M, C,
-                             eps, s));
+    TIMED(GPT2_TIMER_LN_FWD, layernorm_forward(dt, ln1, a.ln1_mean, a.ln1_rstd, x, P + o.ln1_w,
+                                               P + o.ln1_b, M, C, eps, s));
     Epilogue e = epi(EPI_BIAS, a.qkv, 3 * C);
     e.bias = P + o.qkv_b;
     LAUNCH(gemm(dt, true, true, M, 3 * C, C, ln1, C, md->wt(o.qkv_w), C, e, s));
@@ -631,8 +643,8 @@ static int forward_trunk(gpt2_model* md, const int32_t* tokens, const int32_t* t
     e.resid = x;
     e.ldr = C;
     LAUNCH(gemm(dt, true, true, M, C, C, a.atty, C, md->wt(o.proj_w), C, e, s));
-    LAUNCH(layernorm_forward(dt, ln2, a.ln2_mean, a.ln2_rstd, a.res2, P + o.ln2_w, P + o.ln2_b, M,
-                             C, eps, s));
+    TIMED(GPT2_TIMER_LN_FWD, layernorm_forward(dt, ln2, a.ln2_mean, a.ln2_rstd, a.res2,
+                                               P + o.ln2_w, P + o.ln2_b, M, C, eps, s));
     e = epi(EPI_BIAS_GELU, a.fch, 4 * C);
     e.bias = P + o.fc_b;
     e.out2 = fchg;
@@ -645,8 +657,8 @@ static int forward_trunk(gpt2_model* md, const int32_t* tokens, const int32_t* t
     LAUNCH(gemm(dt, true, true, M, C, 4 * C, fchg, 4 * C, md->wt(o.fcp_w), 4 * C, e, s));
     x = a.res3;
   }
-  LAUNCH(layernorm_forward(dt, md->lnf, md->lnf_mean, md->lnf_rstd, x, P + Ly.lnf_w, P + Ly.lnf_b,
-                           M, C, eps, s));
+  TIMED(GPT2_TIMER_LN_FWD, layernorm_forward(dt, md->lnf, md->lnf_mean, md->lnf_rstd, x,
+                                             P + Ly.lnf_w, P + Ly.lnf_b, M, C, eps, s));
   return GPT2_OK;
 }
 
@@ -809,9 +821,10 @@ int gpt2_backward(gpt2_model* md) {
   };
   {
     void* slot = ln_part();
-    LAUNCH(layernorm_backward(dt, top, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
-                              md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
-                              slot, s, &md->cols.back()));
+    TIMED(GPT2_TIMER_LN_BWD,
+          layernorm_backward(dt, top, nullptr, G + Ly.lnf_w, G + Ly.lnf_b, fcp_b_below, false,
+                             md->dbuf_c, xfinal, md->lnf_mean, md->lnf_rstd, P + Ly.lnf_w, M, C,
+                             slot, s, &md->cols.back()));
   }
   AccItem pend[8];
   int npend = 0;
@@ -869,9 +882,10 @@ int gpt2_backward(gpt2_model* md) {
     // mid = d res2 = d res3 + the LayerNorm-2 backward
     {
       void* slot = ln_part();
-      LAUNCH(layernorm_backward(dt, mid, in, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
-                                md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
-                                slot, s, &md->cols.back()));
+      TIMED(GPT2_TIMER_LN_BWD,
+            layernorm_backward(dt, mid, in, G + o.ln2_w, G + o.ln2_b, G + o.proj_b, true,
+                               md->dbuf_c, a.res2, a.ln2_mean, a.ln2_rstd, P + o.ln2_w, M, C,
+                               slot, s, &md->cols.back()));
     }
     // attention output projection: res2 = x + atty proj_w^T + proj_b
     LAUNCH(gemm(dt, true, false, M, C, C, mid, C, md->wt(o.proj_w), C,
@@ -909,14 +923,15 @@ int gpt2_backward(gpt2_model* md) {
           // main stream has produced the inputs
           LAUNCH(hipEventRecord(md->ev_ready[npairs], s));
           LAUNCH(hipStreamWaitEvent(md->side, md->ev_ready[npairs], 0));
-          LAUNCH(gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, md->side));
+          TIMED_ON(GPT2_TIMER_WGRAD_PAIR, md->side,
+                   gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, md->side));
           LAUNCH(hipEventRecord(md->ev_done[npairs], md->side));
           ++npairs;
           pend_pair = npairs - 1;
           pend_sets[0] = (l + 1) % 3;
           pend_sets[1] = l % 3;
         } else {
-          LAUNCH(gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+          TIMED(GPT2_TIMER_WGRAD_PAIR, gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
         }
         npend = 0;
       } else {  // the layer above alone; this one waits for the next
@@ -935,10 +950,11 @@ int gpt2_backward(gpt2_model* md) {
     void* dx = l > 0 ? md->bw_in[(l - 1) % 3] : md->dres;
     {
       void* slot = ln_part();
-      LAUNCH(layernorm_backward(dt, dx, mid, G + o.ln1_w, G + o.ln1_b,
-                                l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c,
-                                xin, a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, slot, s,
-                                &md->cols.back()));
+      TIMED(GPT2_TIMER_LN_BWD,
+            layernorm_backward(dt, dx, mid, G + o.ln1_w, G + o.ln1_b,
+                               l > 0 ? G + Ly.layers[l - 1].fcp_b : nullptr, true, md->dbuf_c,
+                               xin, a.ln1_mean, a.ln1_rstd, P + o.ln1_w, M, C, slot, s,
+                               &md->cols.back()));
     }
   }
   LAUNCH(column_reduce_batched(md->cols.data(), (int)md->cols.size(), s));
@@ -1176,11 +1192,12 @@ int gpt2_load_state(gpt2_model* md, const char* path) {
 
 int gpt2_set_kernel_timer(gpt2_model* md, int which, int max_launches) {
   if (!md) return fail(GPT2_EINVAL, "NULL model");
-  if (which < GPT2_TIMER_NONE || which > GPT2_TIMER_ADAMW)
+  if (which < GPT2_TIMER_NONE || which > GPT2_TIMER_LN_BWD)
     return fail(GPT2_EINVAL, "unknown timer %d", which);
   if (which != GPT2_TIMER_NONE && (max_launches < 1 || max_launches > (1 << 20)))
     return fail(GPT2_EINVAL, "max_launches must be in [1, 2^20]");
   HIP_TRY(hipStreamSynchronize(md->stream));
+  if (md->side) HIP_TRY(hipStreamSynchronize(md->side));
   release_timer(md);
   if (which == GPT2_TIMER_NONE) return GPT2_OK;
   md->timer_ev.resize(2 * (size_t)max_launches);
@@ -1200,6 +1217,7 @@ int gpt2_set_kernel_timer(gpt2_model* md, int which, int max_launches) {
 int gpt2_read_kernel_timer(gpt2_model* md, int* launches, double* total_ms) {
   if (!md || !launches || !total_ms) return fail(GPT2_EINVAL, "NULL argument");
   HIP_TRY(hipStreamSynchronize(md->stream));
+  if (md->side) HIP_TRY(hipStreamSynchronize(md->side));
   double sum = 0.0;
   for (int i = 0; i < md->timer_used; ++i) {
     float ms = 0.f;

@@ -4,10 +4,11 @@
 // section) prints next to the loss and the gradient norm of every step
 // their z-score against the recent steps ("nanz" while there is no history
 // yet), and the run was later restarted with flags that skip an update
-// whose loss or norm z-score exceeds 5 (results section).  This is that
+// whose loss or norm z-score exceeds 5 (400B-token run section).  This is that
 // detector: z of a new value against the mean and (population) standard
 // deviation of the last `window` finite values, in double precision, each
 // recomputed from the window itself so that no running sum drifts.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -43,11 +44,16 @@ int gpt2_zscore_update(gpt2_zscore* zs, double x, double* z_out) {
   const int w = (int)zs->ring.size();
   double z = std::numeric_limits<double>::quiet_NaN();
   if (zs->count == w && std::isfinite(x)) {
+    // sums taken oldest first (the full ring's oldest value is at head), so
+    // that a detector restored by gpt2_zscore_set_state gives the same bits
     double mean = 0.0;
-    for (double v : zs->ring) mean += v;
+    for (int i = 0; i < w; ++i) mean += zs->ring[(size_t)((zs->head + i) % w)];
     mean /= w;
     double var = 0.0;
-    for (double v : zs->ring) var += (v - mean) * (v - mean);
+    for (int i = 0; i < w; ++i) {
+      const double d = zs->ring[(size_t)((zs->head + i) % w)] - mean;
+      var += d * d;
+    }
     const double sd = std::sqrt(var / w);
     if (sd > 0.0) z = (x - mean) / sd;
   }
@@ -57,6 +63,36 @@ int gpt2_zscore_update(gpt2_zscore* zs, double x, double* z_out) {
     if (zs->count < w) ++zs->count;
   }
   if (z_out) *z_out = z;
+  return GPT2_OK;
+}
+
+int gpt2_zscore_get_state(const gpt2_zscore* zs, double* values, int cap, int* window,
+                          int* count) {
+  if (!zs) return gpt2_internal_fail(GPT2_EINVAL, "NULL detector");
+  const int w = (int)zs->ring.size();
+  if (window) *window = w;
+  if (count) *count = zs->count;
+  if (!values) return GPT2_OK;
+  if (cap < zs->count) return gpt2_internal_fail(GPT2_EINVAL, "values holds fewer than count");
+  // oldest first: before the window fills, slots 0 .. count-1 in order;
+  // once full, from `head` around the ring
+  const int start = zs->count == w ? zs->head : 0;
+  for (int i = 0; i < zs->count; ++i) values[i] = zs->ring[(size_t)((start + i) % w)];
+  return GPT2_OK;
+}
+
+int gpt2_zscore_set_state(gpt2_zscore* zs, const double* values, int count) {
+  if (!zs) return gpt2_internal_fail(GPT2_EINVAL, "NULL detector");
+  const int w = (int)zs->ring.size();
+  if (count < 0 || count > w || (count > 0 && !values))
+    return gpt2_internal_fail(GPT2_EINVAL, "count must be in [0, window] with values given");
+  for (int i = 0; i < count; ++i)
+    if (!std::isfinite(values[i]))
+      return gpt2_internal_fail(GPT2_EINVAL, "a window holds finite values only");
+  std::fill(zs->ring.begin(), zs->ring.end(), 0.0);
+  for (int i = 0; i < count; ++i) zs->ring[(size_t)i] = values[i];
+  zs->count = count;
+  zs->head = count % w;
   return GPT2_OK;
 }
 
