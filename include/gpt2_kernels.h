@@ -125,6 +125,24 @@ int gpt2k_attention_backward_colsum(int dtype, void* dev_dqkv, const void* dev_d
                                     const float* dev_lse, int B, int T, int H, int hd,
                                     void* dev_scratch, float* dev_colsum, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gpt2k_attention_backward_colsum without the scratch argument.  The
+ * per-row values the backward keeps between its two passes live in a fixed
+ * device array of 2^20 floats (4 MiB) that the library holds on each GPU it
+ * runs on until the process ends; its address is looked up once per device
+ * on the first call there.  Allocates nothing (no hipMalloc, no allocating
+ * library routine).  Every call on one GPU shares that array: calls that
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * ordered by the caller.  Nothing in the array needs to start at zero (each
+ * call writes every value it reads).  Same arguments, results and errors as
+ * gpt2k_attention_backward_colsum, plus GPT2_EINVAL before anything runs
+ * when B*H*T > 2^20. */
+int gpt2k_attention_backward_noalloc(int dtype, void* dev_dqkv, const void* dev_dout,
+                                     const void* dev_qkv, const void* dev_out,
+                                     const float* dev_lse, int B, int T, int H, int hd,
+                                     float* dev_colsum, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

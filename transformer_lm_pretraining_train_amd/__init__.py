@@ -119,6 +119,7 @@ def lib() -> ctypes.CDLL:
             "gpt2k_attention_backward": (I, [I, P, P, P, P, P, I, I, I, I, P, P]),
             "gpt2k_attention_colsum_ok": (I, [I, I]),
             "gpt2k_attention_backward_colsum": (I, [I, P, P, P, P, P, I, I, I, I, P, P, P]),
+            "gpt2k_attention_backward_noalloc": (I, [I, P, P, P, P, P, I, I, I, I, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -445,6 +446,15 @@ def attention_backward(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, scratch, s
     _check(lib().gpt2k_attention_backward_colsum(dtype, _ptr(dqkv), _ptr(dout), _ptr(qkv),
                                                  _ptr(out), _ptr(lse), B, T, H, hd,
                                                  _ptr(scratch), _ptr(colsum), _stream(stream)))
+
+
+def attention_backward_noalloc(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd, stream=None,
+                               colsum=None):
+    """gpt2k_attention_backward_noalloc: the attention backward with its
+    per-row scratch in the library's fixed device array (no allocation)."""
+    _check(lib().gpt2k_attention_backward_noalloc(dtype, _ptr(dqkv), _ptr(dout), _ptr(qkv),
+                                                  _ptr(out), _ptr(lse), B, T, H, hd, _ptr(colsum),
+                                                  _stream(stream)))
 
 
 def attention_colsum_ok(dtype, hd):

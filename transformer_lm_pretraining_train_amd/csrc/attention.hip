@@ -13,8 +13,18 @@
 //   pass 1 (per query i): D_i = sum_d dO_i O_i, dQ_i = scale sum_j dS_ij k_j
 //   pass 2 (per key j):   dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij q_i
 // with dS_ij = P_ij (dO_i . v_j - D_i).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
+
+// Fixed device-resident scratch for the attention backward's entry point
+// that allocates nothing (attention_backward_noalloc): the per-row values
+// D = rowsum(dO * O) the dQ pass writes and the dK/dV pass reads.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never passes this name to a kernel: it is a host-side stand-in, not a
+// device address; the address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) float scratch[gk::kNoAllocAttnScratchFloats];
 
 namespace gk {
 
@@ -318,6 +328,36 @@ hipError_t attention_backward(int dt, void* dqkv, const void* dout, const void* 
     AT_DISPATCH_HD(hd, launch_bwd, dqkv, Dbuf, dout, qkv, out, lse, B, Tn, H, s);
   }
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+static hipError_t noalloc_scratch(float** out) {
+  static std::mutex mu;
+  static float* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = (float*)p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t attention_backward_noalloc(int dt, void* dqkv, const void* dout, const void* qkv,
+                                      const void* out, const float* lse, int B, int Tn, int H,
+                                      int hd, hipStream_t s, float* colsum) {
+  if ((int64_t)B * H * Tn > (int64_t)kNoAllocAttnScratchFloats) return hipErrorInvalidValue;
+  float* D = nullptr;
+  const hipError_t e = noalloc_scratch(&D);
+  if (e != hipSuccess) return e;
+  return attention_backward(dt, dqkv, dout, qkv, out, lse, B, Tn, H, hd, D, s, colsum);
 }
 
 }  // namespace gk

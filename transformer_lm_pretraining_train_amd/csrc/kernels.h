@@ -83,6 +83,15 @@ inline int attention_colsum_blocks(int B, int T) { return B * ((T + 127) / 128);
 hipError_t attention_backward(int dt, void* dqkv, const void* dout, const void* qkv,
                               const void* out, const float* lse, int B, int T, int H, int hd,
                               void* scratch, hipStream_t s, float* colsum = nullptr);
+// The same without a scratch argument: D lives in a fixed device array of
+// kNoAllocAttnScratchFloats floats (one per GPU, kept until the process
+// ends; calls that overlap on one GPU race on it).  hipErrorInvalidValue
+// when B*H*T exceeds it.  Allocates nothing.
+constexpr int kNoAllocAttnScratchFloats = 1 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t attention_backward_noalloc(int dt, void* dqkv, const void* dout, const void* qkv,
+                                      const void* out, const float* lse, int B, int T, int H,
+                                      int hd, hipStream_t s, float* colsum);
 
 // ---- GEMM: C(m, n) = sum_k A(m, k) B(n, k), then an epilogue.
 // a_kmajor: A(m,k) = A[m*lda + k], else A[k*lda + m]; likewise b_kmajor for

@@ -156,4 +156,26 @@ int gpt2k_attention_backward_colsum(int dtype, void* dqkv, const void* dout, con
                    "attention_backward");
 }
 
+int gpt2k_attention_backward_noalloc(int dtype, void* dqkv, const void* dout, const void* qkv,
+                                     const void* out, const float* lse, int B, int T, int H,
+                                     int hd, float* colsum, void* stream) {
+  if (colsum && !attention_colsum_ok(dtype, hd))
+    return gpt2_internal_fail(GPT2_EINVAL, "column sums not available for this dtype / head size");
+  if (dtype != GPT2_FP32 && dtype != GPT2_BF16)
+    return gpt2_internal_fail(GPT2_EINVAL, "dtype must be 0 or 1");
+  if (!dqkv || !dout || !qkv || !out || !lse || B < 1 || T < 1 || H < 1)
+    return gpt2_internal_fail(GPT2_EINVAL, "bad argument");
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return gpt2_internal_fail(GPT2_EINVAL, "head size must be 16, 32, 64 or 128");
+  if ((int64_t)B * H * T > (int64_t)kNoAllocAttnScratchFloats) {
+    char msg[160];
+    snprintf(msg, sizeof(msg), "B*H*T = %lld exceeds the fixed scratch of %d rows (4 MiB)",
+             (long long)B * H * T, kNoAllocAttnScratchFloats);
+    return gpt2_internal_fail(GPT2_EINVAL, msg);
+  }
+  return launch_rc(attention_backward_noalloc(dtype, dqkv, dout, qkv, out, lse, B, T, H, hd,
+                                              (hipStream_t)stream, colsum),
+                   "attention_backward_noalloc");
+}
+
 }  // extern "C"
