@@ -385,9 +385,17 @@ constexpr uint32_t kOOB = 0x80000000u;
 // their zeros.
 //  k-major source: [row][64 k], 128-byte rows, 16-byte chunks XOR-swizzled
 //    by row (conflict-free 16-byte fragment reads).
-//  m-major source: [64 k][R rows] as in memory, the chunks of k-row k
-//    rotated by 4*(k%4) (so the four k-rows of a transposing read hit
-//    different banks); fragments via ds_read_b64_tr_b16.  R >= 128.
+//  m-major source: [64 k][R rows] as in memory, the chunks of each k-row
+//    permuted so that the four k-rows of a transposing read land on four
+//    different quarters of the 64 LDS banks; fragments via
+//    ds_read_b64_tr_b16.  R >= 128.  A read takes 64 bytes (four 16-byte
+//    chunks) of each of four k-rows; with R = 128 or 256 the rows are
+//    pitched at a multiple of 256 bytes and rotating k-row k by 4*(k%4)
+//    chunks spreads them; with R = 192 (384-byte rows, an odd multiple of
+//    128 bytes) consecutive rows already differ by half the banks, and
+//    swapping the 4-chunk groups of the k-rows with bit 1 set (chunk ^ 4)
+//    completes the spread where a rotation modulo 24 chunks would wrap onto
+//    used banks.
 template <int R, bool KMAJOR, int NW>
 struct BigOperand {
   static constexpr int ELEMS = R * 64;
@@ -395,8 +403,14 @@ struct BigOperand {
   static constexpr int NI = R * 8 / (64 * NW);  // load instructions per wave per tile
 
   // physical chunk of logical chunk lc in k-row krow, and the inverse
-  __device__ __forceinline__ static int mphys(int krow, int lc) { return (lc + CPR - 4 * (krow & 3)) % CPR; }
-  __device__ __forceinline__ static int mlog(int krow, int p) { return (p + 4 * (krow & 3)) % CPR; }
+  __device__ __forceinline__ static int mphys(int krow, int lc) {
+    if constexpr (CPR == 24) return lc ^ (krow & 2 ? 4 : 0);
+    else return (lc + CPR - 4 * (krow & 3)) % CPR;
+  }
+  __device__ __forceinline__ static int mlog(int krow, int p) {
+    if constexpr (CPR == 24) return p ^ (krow & 2 ? 4 : 0);
+    else return (p + 4 * (krow & 3)) % CPR;
+  }
 
   struct Src {
     __amdgpu_buffer_rsrc_t rs;
