@@ -27,8 +27,9 @@ METRIC = "train tokens/sec + MFU, GPT-2 124M bf16 B×T=16×1024, 1 MI355X"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of one launch of the dominant kernel (the weight gradients of
-# two layers, gemm_big_kernel<256,256,false,false,EPI_ACC_F32>, 216 tiles)
+# HBM traffic of one launch of the dominant kernel (at GPT-2 124M the weight
+# gradients of two layers, gemm_big_kernel<256,256,false,false,EPI_ACC_F32>,
+# 216 tiles)
 # from two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then
 # WRITE_SIZE, KiB per dispatch, mean over the timed pairs), each scaled by
 # what the same counter reads for a plain device copy of known size.  Valid
@@ -64,39 +65,43 @@ def parse():
     return ap.parse_args()
 
 
-def wgrad_pair_flops(cfg):
-    """Algorithmic flops of one launch of two layers' weight gradients:
-    dW += dy^T x for fc-proj (C x 4C), fc (4C x C), proj (C x C) and qkv
-    (3C x C) of each layer, K = B*T tokens: 2 * 2 * B*T * 12 C^2."""
+def wgrad_layer_flops(cfg):
+    """Algorithmic flops of one layer's weight gradients: dW += dy^T x for
+    fc-proj (C x 4C), fc (4C x C), proj (C x C) and qkv (3C x C), K = B*T
+    tokens: 2 * B*T * 12 C^2."""
     C, M = cfg.n_embd, cfg.micro_batch * cfg.seq_len
-    return 2.0 * 2 * M * 12 * C * C
+    return 2.0 * M * 12 * C * C
 
 
-def wgrad_pair_roofline(cfg, n, total_ms):
-    """Roofline entry for the dominant kernel of the step: the grouped launch
-    of two layers' weight gradients (eight products, one 256 x 256 tile per
-    workgroup, fp32 accumulation into the gradients), which runs on the
-    library's second stream beside the next layer's input-gradient work.
-    Duration from the library's event pairs around each such launch inside
-    the timed steps."""
+def wgrad_roofline(cfg, n, total_ms, micro_steps):
+    """Roofline entry for the dominant kernel of the step: the grouped
+    launches of the layers' weight gradients (the four products of one layer
+    or of two layers per launch, one 256 x 256 tile per workgroup, fp32
+    accumulation into the gradients; at GPT-2 124M two layers per launch, on
+    the library's second stream beside the next layer's input-gradient work).
+    Every such launch of the timed steps is bracketed by the library's event
+    pairs; the flops per launch are the timed layers' flops over the
+    launches."""
     import hashlib
-    C, M = cfg.n_embd, cfg.micro_batch * cfg.seq_len
-    t = total_ms / 1e3 / max(n, 1)
-    flops = wgrad_pair_flops(cfg)
+    C, M, L = cfg.n_embd, cfg.micro_batch * cfg.seq_len, cfg.n_layer
+    n = max(n, 1)
+    t = total_ms / 1e3 / n
+    layers = L * micro_steps / n  # layers per launch
+    flops = wgrad_layer_flops(cfg) * layers
     achieved = flops / t / 1e12
     # per layer: the bf16 operands dy and x of the four products, read once
     # (columns C + 4C, 4C + C, C + C, 3C + C: 16 C per token), and the 12 C^2
     # fp32 gradients, read and written
-    alg = 2 * (2 * M * 16 * C + 8 * 12 * C * C)
+    alg = int(layers * (2 * M * 16 * C + 8 * 12 * C * C))
     traffic = None
     src = os.path.join(ROOT, "transformer_lm_pretraining_train_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     tr = WGRAD_TRAFFIC
-    if tr and sha == tr["gemm_source_sha256_16"] and (M, C) == tuple(tr["shape"]):
+    if tr and sha == tr["gemm_source_sha256_16"] and (M, C) == tuple(tr["shape"]) and layers == 2:
         traffic = int(tr["fetch_kib"] * 1024 * tr["fetch_factor"]
                       + tr["write_kib"] * 1024 * tr["write_factor"])
-    return {"kernel": "gemm_big_kernel<256,256,false,false,EPI_ACC_F32> (weight gradients of two "
-                      f"layers: 8 products, K={M}, {2 * 12 * C * C} outputs)",
+    return {"kernel": "gemm_big_kernel<256,256,false,false,EPI_ACC_F32> (grouped weight gradients, "
+                      f"{layers:g} layer(s) per launch: {4 * layers:g} products, K={M})",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
             "traffic_unit": "bytes per launch", "algorithmic_bytes": alg,
@@ -255,7 +260,7 @@ def main():
             log(f"warmup step {s + 1}: loss {losses.mean().item():.4f} norm {norm.item():.4f}")
         stream.synchronize()
         if not args.no_roofline:
-            model.set_kernel_timer("wgrad_pair", args.steps * wl.grad_accum * (wl.n_layer // 2 + 1))
+            model.set_kernel_timer("wgrad", args.steps * wl.grad_accum * wl.n_layer)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -275,7 +280,7 @@ def main():
 
     roof = others = None
     if not args.no_roofline:
-        roof = wgrad_pair_roofline(cfg, *model.read_kernel_timer())
+        roof = wgrad_roofline(cfg, *model.read_kernel_timer(), args.steps * wl.grad_accum)
         log(f"roofline: {roof}")
         # one more step per timed kernel, outside the timed region
         timed = {}

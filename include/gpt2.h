@@ -315,9 +315,10 @@ int gpt2_debug_read(gpt2_model* model, int which, int layer, void* dev_dst, size
  *   CE_FWD       the fused softmax cross-entropy of each forward with targets
  *                (loss, lse, argmax and the logit gradient)
  *   ADAMW        the AdamW update of each optimizer step (not the norm)
- *   WGRAD_PAIR   each launch of the weight gradients of two layers (eight
- *                products, bf16), on the stream it runs on (the library's
- *                second stream when it has one)
+ *   WGRAD        each grouped launch of the layers' weight gradients (the
+ *                four products of one layer, or of two layers as one
+ *                launch), on the stream it runs on (the library's second
+ *                stream for most two-layer launches)
  *   LN_FWD       every LayerNorm forward of the forward pass
  *   LN_BWD       every LayerNorm backward of the backward pass */
 enum {
@@ -327,7 +328,7 @@ enum {
   GPT2_TIMER_ATTN_BWD = 3,
   GPT2_TIMER_CE_FWD = 4,
   GPT2_TIMER_ADAMW = 5,
-  GPT2_TIMER_WGRAD_PAIR = 6,
+  GPT2_TIMER_WGRAD = 6,
   GPT2_TIMER_LN_FWD = 7,
   GPT2_TIMER_LN_BWD = 8
 };

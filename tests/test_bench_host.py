@@ -21,22 +21,26 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_wgrad_pair_roofline_arithmetic():
-    """Two GPT-2 124M layers' weight gradients: 2 x 2 x 16384 x 12 x 768^2
-    = 463.9 GFLOP per launch; bytes: the bf16 operands (16 C columns per
-    token per layer) and the fp32 gradients read and written."""
+def test_wgrad_roofline_arithmetic():
+    """Two GPT-2 124M layers' weight gradients per launch (12 layers, six
+    launches per micro-step): 2 x 2 x 16384 x 12 x 768^2 = 463.9 GFLOP per
+    launch; bytes: the bf16 operands (16 C columns per token per layer) and
+    the fp32 gradients read and written.  350M: one layer per launch."""
     cfg = g.config_for(synth.workload("gpt2_124m"))
-    r = bench.wgrad_pair_roofline(cfg, 4, 4 * 0.5)  # four launches of 0.5 ms
+    r = bench.wgrad_roofline(cfg, 12, 12 * 0.5, 2)  # two micro-steps, twelve launches of 0.5 ms
     M, C = 16384, 768
     flops = 2 * 2 * M * 12 * C * C
     assert r["flops_per_launch"] == flops and abs(flops - 463.9e9) < 0.1e9
     assert r["achieved"] == pytest.approx(flops / 0.5e-3 / 1e12, rel=1e-4)
     assert r["peak"] == 2516.6 and r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
-    assert r["avg_launch_us"] == 500.0 and r["launches_timed"] == 4
+    assert r["avg_launch_us"] == 500.0 and r["launches_timed"] == 12
     assert r["algorithmic_bytes"] == 2 * (2 * M * 16 * C + 8 * 12 * C * C)
     if r["traffic"] is not None:  # counters taken on this GEMM source
         assert r["traffic"] > 0
+    c350 = g.config_for(synth.workload("gpt2_350m"))
+    r = bench.wgrad_roofline(c350, 48, 48 * 0.5, 2)  # 24 layers, one per launch
+    assert r["flops_per_launch"] == 2 * 16384 * 12 * 1024 ** 2 and r["traffic"] is None
 
 
 def test_other_kernels_arithmetic():

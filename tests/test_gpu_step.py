@@ -363,14 +363,15 @@ def test_kernel_timer_counts_launches_and_leaves_results_unchanged():
 
 
 def test_kernel_timer_second_stream_and_layernorm_slots():
-    """The weight-gradient pair timer (events on the library's second stream
-    for six bf16 layers: pairs 5-4, 3-2 and 1-0) and the LayerNorm timers
-    (2 L + 1 launches per forward and per backward) count every launch of a
+    """The weight-gradient timer (events on the library's second stream for
+    six bf16 layers: pairs 5-4, 3-2 and 1-0; five layers: pairs 4-3 and 2-1,
+    then layer 0 alone on the main stream) and the LayerNorm timers (2 L + 1
+    launches per forward and per backward) count every launch of a
     two-micro-step step and leave the result bit-identical."""
     wl, cfg, ocfg, layout, flat, batches = setup_case("small", "bf16", k=2)
     _, ref = gpu_step(cfg, flat, batches)
     L = wl.n_layer
-    for name, per_micro in (("wgrad_pair", L // 2), ("ln_fwd", 2 * L + 1), ("ln_bwd", 2 * L + 1)):
+    for name, per_micro in (("wgrad", L // 2), ("ln_fwd", 2 * L + 1), ("ln_bwd", 2 * L + 1)):
         m = g.Model(cfg)
         m.set_params(to_dev(flat))
         m.set_kernel_timer(name, 1000)
@@ -379,6 +380,13 @@ def test_kernel_timer_second_stream_and_layernorm_slots():
         assert n == per_micro * len(batches) and ms > 0.0, (name, n, ms)
         assert np.array_equal(out[0]["params"], ref[0]["params"]), name
         m.close()
+    wl5, cfg5, _, _, flat5, batches5 = setup_case("small", "bf16", k=2, n_layer=5)
+    m = g.Model(cfg5)
+    m.set_params(to_dev(flat5))
+    m.set_kernel_timer("wgrad", 1000)
+    gpu_step(cfg5, flat5, batches5, model=m)
+    assert m.read_kernel_timer()[0] == 3 * len(batches5)
+    m.close()
 
 
 def test_gradients_bitwise_repeatable():

@@ -33,7 +33,7 @@ EPI = {"store": 0, "bias": 1, "bias_resid": 2, "bias_gelu": 3, "gelu_bwd": 4, "a
 DBG = {"logits": 0, "losses": 1, "argmax": 2, "ln1": 3, "qkv": 4, "atty": 5, "res2": 6,
        "fch": 7, "res3": 8, "lnf": 9, "att_lse": 10, "encoded": 11}
 TIMER = {"none": 0, "lm_head_fwd": 1, "attn_fwd": 2, "attn_bwd": 3, "ce_fwd": 4, "adamw": 5,
-         "wgrad_pair": 6, "ln_fwd": 7, "ln_bwd": 8}
+         "wgrad": 6, "ln_fwd": 7, "ln_bwd": 8}
 
 
 class GPT2Config(ctypes.Structure):

@@ -923,7 +923,7 @@ int gpt2_backward(gpt2_model* md) {
           // main stream has produced the inputs
           LAUNCH(hipEventRecord(md->ev_ready[npairs], s));
           LAUNCH(hipStreamWaitEvent(md->side, md->ev_ready[npairs], 0));
-          TIMED_ON(GPT2_TIMER_WGRAD_PAIR, md->side,
+          TIMED_ON(GPT2_TIMER_WGRAD, md->side,
                    gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, md->side));
           LAUNCH(hipEventRecord(md->ev_done[npairs], md->side));
           ++npairs;
@@ -931,17 +931,17 @@ int gpt2_backward(gpt2_model* md) {
           pend_sets[0] = (l + 1) % 3;
           pend_sets[1] = l % 3;
         } else {
-          TIMED(GPT2_TIMER_WGRAD_PAIR, gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+          TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
         }
         npend = 0;
       } else {  // the layer above alone; this one waits for the next
-        LAUNCH(gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
         std::copy(pend + 4, pend + 8, pend);
         npend = 4;
       }
     }
     if (l == 0 && npend > 0) {
-      LAUNCH(gemm_acc_group(dt, npend, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+      TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, npend, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
       npend = 0;
     }
     // d x = d res2 + the LayerNorm-1 backward, into the next layer's input
