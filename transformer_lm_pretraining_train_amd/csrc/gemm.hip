@@ -609,14 +609,17 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
   typename OB::Src srcB;
   OA::init(srcA, A, lda, m0, M, K, wave, lane);
   OB::init(srcB, B, ldb, n0, N, K, wave, lane);
+  auto issueA = [&](bf16* st, int k0) {
+    if (k0 + 64 > kend) OA::template load<true>(st, srcA, lda, k0, kend, wave, lane);
+    else OA::template load<false>(st, srcA, lda, k0, kend, wave, lane);
+  };
+  auto issueB = [&](bf16* st, int k0) {
+    if (k0 + 64 > kend) OB::template load<true>(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
+    else OB::template load<false>(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
+  };
   auto issue = [&](bf16* st, int k0) {
-    if (k0 + 64 > kend) {
-      OA::template load<true>(st, srcA, lda, k0, kend, wave, lane);
-      OB::template load<true>(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
-    } else {
-      OA::template load<false>(st, srcA, lda, k0, kend, wave, lane);
-      OB::template load<false>(st + OA::ELEMS, srcB, ldb, k0, kend, wave, lane);
-    }
+    issueA(st, k0);
+    issueB(st, k0);
   };
   // Fragments are double-buffered in registers: the LDS reads of k-step s+1
   // are issued between the MFMAs of k-step s.
@@ -639,10 +642,30 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
   // iteration kt multiplies the tile in `cur` while the next tile streams
-  // into `nxt`; one barrier per k-tile.
+  // into `nxt`; one barrier per k-tile.  Where the next tile's loads are
+  // issued: a wave whose loads back up in the address path stalls there
+  // before its MFMAs, so the two waves of a SIMD should not both issue
+  // theirs at one moment when the loads are slow to drain (measured on the
+  // three operand orientations of the step's products):
+  //   k-major x k-major: every wave at the top of the iteration;
+  //   k-major x m-major: A's loads at the top, B's after k-step 0
+  //     (the head's 256-wide d lnf product 4 % faster, 192-wide products
+  //     unchanged);
+  //   m-major x m-major: waves 0 .. NW/2-1 (one per SIMD) at the top, the
+  //     others after k-step 1 (weight gradients 11-12 % faster).
+  constexpr int kPlace = AKM ? (BKM ? 0 : 1) : 2;
+  const bool early = wave < NW / 2;
   auto iter = [&](int kt, bf16* cur, bf16* nxt) {
-    if (kt + 1 < nk) issue(nxt, kbeg + (kt + 1) * 64);
-    // keep the loads at the top: the scheduler would otherwise sink them
+    const bool more = kt + 1 < nk;
+    const int k1 = kbeg + (kt + 1) * 64;
+    if constexpr (kPlace == 0) {
+      if (more) issue(nxt, k1);
+    } else if constexpr (kPlace == 1) {
+      if (more) issueA(nxt, k1);
+    } else {
+      if (more && early) issue(nxt, k1);
+    }
+    // keep the loads in place: the scheduler would otherwise sink them
     // below the math, next to the wait that ends the iteration
     __builtin_amdgcn_sched_barrier(0);
     bf16x8_t fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
@@ -652,10 +675,18 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);  // all reads of k-steps 0 and 1
     __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);  // then the MFMAs of k-step 0
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPlace == 1) {
+      if (more) issueB(nxt, k1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     frags(cur, 2, fa0, fb0);
     mma(fa1, fb1);
     interleave_mfma_reads<TI * TJ, NR>();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPlace == 2) {
+      if (more && !early) issue(nxt, k1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     frags(cur, 3, fa1, fb1);
     mma(fa0, fb0);
     interleave_mfma_reads<TI * TJ, NR>();
