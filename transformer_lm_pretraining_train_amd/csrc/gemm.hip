@@ -652,7 +652,8 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
   //     (the head's 256-wide d lnf product 4 % faster, 192-wide products
   //     unchanged);
   //   m-major x m-major: waves 0 .. NW/2-1 (one per SIMD) at the top, the
-  //     others after k-step 1 (weight gradients 11-12 % faster).
+  //     others after k-step 2 (weight gradients 13-15 % faster; after
+  //     k-step 1: 11-12 %; every wave at k-step 0 or A and B apart: slower).
   constexpr int kPlace = AKM ? (BKM ? 0 : 1) : 2;
   const bool early = wave < NW / 2;
   auto iter = [&](int kt, bf16* cur, bf16* nxt) {
@@ -683,14 +684,14 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
     mma(fa1, fb1);
     interleave_mfma_reads<TI * TJ, NR>();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kPlace == 2) {
-      if (more && !early) issue(nxt, k1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     frags(cur, 3, fa1, fb1);
     mma(fa0, fb0);
     interleave_mfma_reads<TI * TJ, NR>();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kPlace == 2) {
+      if (more && !early) issue(nxt, k1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mma(fa1, fb1);
     wait_vmem();
     __syncthreads();
