@@ -114,6 +114,35 @@ def test_tiny_fp32_two_steps_match_oracle():
     assert gs[-1]["step"] == 2
 
 
+def test_tiny_fp32_step_from_a_restored_optimizer_state():
+    """gpt2_set_opt_state: a non-zero AdamW state (m, v, step 5) reads back
+    bit for bit, and the next optimizer step from it -- bias corrections at
+    t = 6, the clip, decay only on the matrices -- matches the oracle's
+    train_step started from the same state (wiki notes, training recipe:
+    AdamW 0.9 / 0.95 / 1e-8, weight decay 0.1, global clip 1.0)."""
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "fp32")
+    rng = np.random.default_rng(11)
+    m0 = (1e-3 * rng.standard_normal(flat.size)).astype(np.float32)
+    v0 = (1e-6 * np.abs(rng.standard_normal(flat.size))).astype(np.float32)
+    print("tiny fp32: step from a restored optimizer state (t = 5)", flush=True)
+    m = g.Model(cfg)
+    m.set_params(to_dev(flat))
+    m.set_opt_state(to_dev(m0), to_dev(v0), 5)
+    mm, vv, t = m.get_opt_state()
+    torch.cuda.synchronize()
+    assert t == 5
+    assert np.array_equal(host(mm), m0) and np.array_equal(host(vv), v0)
+    _, gs = gpu_step(cfg, flat, batches, model=m)
+    p, mo, vo = flat.copy(), m0.copy(), v0.copy()
+    r = oracle.train_step(ocfg, p, mo, vo, 5, batches, LR)
+    gr = gs[0]
+    assert r["t"] == 6 and gr["step"] == 6
+    assert rel_l2(gr["grads"], r["grads"]) <= 1e-3
+    assert rel_l2(gr["m"], mo) <= 1e-3
+    assert rel_l2(gr["v"], vo) <= 1e-3
+    assert rel_l2(gr["params"] - flat, p - flat) <= 2e-2
+
+
 def test_tiny_fp32_grad_accumulation_k3():
     wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "fp32", k=3, B=4)
     print("tiny fp32 k=3", flush=True)
