@@ -532,7 +532,7 @@ int gpt2_create(const gpt2_config* cfg, void* dev_workspace, size_t bytes, void*
   }
   // side stream (default priority) and its events: host-side objects only
   if (md->dt == BF16 && md->L >= 4) {
-    const int np = md->L / 2 + 1;
+    const int np = md->L + 1;  // at most one side-stream group per layer
     e = hipStreamCreateWithFlags(&md->side, hipStreamNonBlocking);
     md->ev_ready.assign(np, nullptr);
     md->ev_done.assign(np, nullptr);
@@ -807,18 +807,46 @@ int gpt2_backward(gpt2_model* md) {
   // before it writes either of the pair's buffer sets again.  A pair that
   // ends at layer 1 of an odd-depth model runs on the main stream, since the
   // four products of layer 0 after it take the same split-K workspace.
+  // Where two layers do not fit one round (wider models) but one layer's
+  // four products do without a K split (GPT-2 350M: 192 tiles), each such
+  // group runs on the side stream the same way, beside the next layer.
   const int Lh = md->L;
   void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 3] : md->dres;
-  int pend_pair = -1;  // pair running on the side stream whose sets are not yet reusable
-  int pend_sets[2] = {-1, -1};
-  int npairs = 0;
+  // groups running on the side stream whose buffer sets are not yet
+  // reusable, oldest first: event index and the sets they read
+  struct SideGroup {
+    int ev, sets[2];
+  };
+  constexpr int kSidePend = 8;  // the three-set rotation keeps at most ~3 pending
+  SideGroup side_pend[kSidePend];
+  int nside = 0;
+  int npairs = 0;  // side-stream groups launched so far (event index)
   auto guard = [&](int set) -> hipError_t {  // main stream: set `set` is about to be written
-    if (pend_pair >= 0 && (pend_sets[0] == set || pend_sets[1] == set)) {
-      pend_pair = -1;
-      return hipStreamWaitEvent(s, md->ev_done[npairs - 1], 0);
+    // wait for the newest group that reads `set`; the side stream runs in
+    // order, so the groups before it are done then too
+    for (int i = nside - 1; i >= 0; --i) {
+      if (side_pend[i].sets[0] == set || side_pend[i].sets[1] == set) {
+        const int ev = side_pend[i].ev;
+        for (int j = i + 1; j < nside; ++j) side_pend[j - i - 1] = side_pend[j];
+        nside -= i + 1;
+        return hipStreamWaitEvent(s, md->ev_done[ev], 0);
+      }
     }
     return hipSuccess;
   };
+  // launch n_ queued products reading buffer sets s0_ and s1_ (-1: none) on
+  // the side stream, once the main stream has produced their inputs
+#define SIDE_LAUNCH(n_, s0_, s1_)                                                               \
+  do {                                                                                          \
+    if (nside == kSidePend) LAUNCH(guard(side_pend[0].sets[0]));                                \
+    LAUNCH(hipEventRecord(md->ev_ready[npairs], s));                                            \
+    LAUNCH(hipStreamWaitEvent(md->side, md->ev_ready[npairs], 0));                              \
+    TIMED_ON(GPT2_TIMER_WGRAD, md->side,                                                        \
+             gemm_acc_group(dt, (n_), pend, M, md->gemm_ws, md->gemm_ws_bytes, md->side));      \
+    LAUNCH(hipEventRecord(md->ev_done[npairs], md->side));                                      \
+    side_pend[nside++] = SideGroup{npairs, {(s0_), (s1_)}};                                     \
+    ++npairs;                                                                                   \
+  } while (0)
   {
     void* slot = ln_part();
     TIMED(GPT2_TIMER_LN_BWD,
@@ -828,6 +856,12 @@ int gpt2_backward(gpt2_model* md) {
   }
   AccItem pend[8];
   int npend = 0;
+  // one layer's four products on the side stream: they fit one round of
+  // tiles without a K split (so they take no workspace)
+  auto single_fits_side = [&]() {
+    return md->side != nullptr && npairs < (int)md->ev_done.size() &&
+           gemm_acc_group_splits(dt, 4, pend, M) == 1;
+  };
   for (int l = Lh - 1; l >= 0; --l) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
@@ -919,29 +953,28 @@ int gpt2_backward(gpt2_model* md) {
     if (npend == 8) {
       if (gemm_acc_group_splits(dt, 8, pend, M) > 0) {  // both layers in one round of tiles
         if (md->side && l != 1 && npairs < (int)md->ev_done.size()) {
-          // beside the next layer's work: the side stream starts once the
-          // main stream has produced the inputs
-          LAUNCH(hipEventRecord(md->ev_ready[npairs], s));
-          LAUNCH(hipStreamWaitEvent(md->side, md->ev_ready[npairs], 0));
-          TIMED_ON(GPT2_TIMER_WGRAD, md->side,
-                   gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, md->side));
-          LAUNCH(hipEventRecord(md->ev_done[npairs], md->side));
-          ++npairs;
-          pend_pair = npairs - 1;
-          pend_sets[0] = (l + 1) % 3;
-          pend_sets[1] = l % 3;
+          // beside the next layer's work
+          SIDE_LAUNCH(8, (l + 1) % 3, l % 3);
         } else {
           TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
         }
         npend = 0;
       } else {  // the layer above alone; this one waits for the next
-        TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        if (single_fits_side()) {
+          SIDE_LAUNCH(4, (l + 1) % 3, -1);
+        } else {
+          TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+        }
         std::copy(pend + 4, pend + 8, pend);
         npend = 4;
       }
     }
     if (l == 0 && npend > 0) {
-      TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, npend, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+      if (npend == 4 && single_fits_side()) {
+        SIDE_LAUNCH(4, 0, -1);
+      } else {
+        TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, npend, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
+      }
       npend = 0;
     }
     // d x = d res2 + the LayerNorm-1 backward, into the next layer's input
@@ -957,6 +990,7 @@ int gpt2_backward(gpt2_model* md) {
                                &md->cols.back()));
     }
   }
+#undef SIDE_LAUNCH
   LAUNCH(column_reduce_batched(md->cols.data(), (int)md->cols.size(), s));
   // embeddings
   LAUNCH(encoder_backward_wte(dt, G + Ly.wte, md->dres, md->tokens, M, C, md->V, md->scratch, s));
