@@ -804,12 +804,12 @@ int gpt2_backward(gpt2_model* md) {
   // time).  Such a pair runs on the side stream, beside the next layer's
   // work (the pair of the first two layers beside the embedding and the
   // remaining bias and LayerNorm gradients); the main stream waits for it
-  // before it writes either of the pair's buffer sets again.  A pair that
-  // ends at layer 1 of an odd-depth model runs on the main stream, since the
-  // four products of layer 0 after it take the same split-K workspace.
-  // Where two layers do not fit one round (wider models) but one layer's
-  // four products do without a K split (GPT-2 350M: 192 tiles), each such
-  // group runs on the side stream the same way, beside the next layer.
+  // before it writes either of the pair's buffer sets again.  Where two
+  // layers do not fit one round (wider models), each layer's four run on the
+  // side stream the same way, beside the next layer: one launch when they fit
+  // a round (GPT-2 350M: 192 tiles), else one per product with its own K
+  // split.  All of them run on the side stream, in order, so that it alone
+  // uses the split-K workspace.
   const int Lh = md->L;
   void* top = Lh > 0 ? md->bw_in[(Lh - 1) % 3] : md->dres;
   // groups running on the side stream whose buffer sets are not yet
@@ -856,12 +856,9 @@ int gpt2_backward(gpt2_model* md) {
   }
   AccItem pend[8];
   int npend = 0;
-  // one layer's four products on the side stream: they fit one round of
-  // tiles without a K split (so they take no workspace)
-  auto single_fits_side = [&]() {
-    return md->side != nullptr && npairs < (int)md->ev_done.size() &&
-           gemm_acc_group_splits(dt, 4, pend, M) == 1;
-  };
+  // with a side stream every weight-gradient launch goes there, in order,
+  // so that it alone uses the split-K workspace
+  auto on_side = [&]() { return md->side != nullptr && npairs < (int)md->ev_done.size(); };
   for (int l = Lh - 1; l >= 0; --l) {
     const LayerOffsets& o = Ly.layers[l];
     LayerAct& a = md->act[l];
@@ -952,15 +949,14 @@ int gpt2_backward(gpt2_model* md) {
     npend += 4;
     if (npend == 8) {
       if (gemm_acc_group_splits(dt, 8, pend, M) > 0) {  // both layers in one round of tiles
-        if (md->side && l != 1 && npairs < (int)md->ev_done.size()) {
-          // beside the next layer's work
+        if (on_side()) {  // beside the next layer's work
           SIDE_LAUNCH(8, (l + 1) % 3, l % 3);
         } else {
           TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 8, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
         }
         npend = 0;
       } else {  // the layer above alone; this one waits for the next
-        if (single_fits_side()) {
+        if (on_side()) {
           SIDE_LAUNCH(4, (l + 1) % 3, -1);
         } else {
           TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, 4, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
@@ -970,7 +966,7 @@ int gpt2_backward(gpt2_model* md) {
       }
     }
     if (l == 0 && npend > 0) {
-      if (npend == 4 && single_fits_side()) {
+      if (npend == 4 && on_side()) {
         SIDE_LAUNCH(4, 0, -1);
       } else {
         TIMED(GPT2_TIMER_WGRAD, gemm_acc_group(dt, npend, pend, M, md->gemm_ws, md->gemm_ws_bytes, s));
