@@ -208,9 +208,9 @@ def test_small_bf16_step_matches_oracle():
 
 
 def test_small_bf16_odd_depth_matches_oracle():
-    """Five layers in bf16: the weight-gradient pair of layers 4-3 on the
-    second stream, of layers 2-1 on the main stream, layer 0's four products
-    alone after it."""
+    """Five layers in bf16: the weight-gradient pairs of layers 4-3 and 2-1,
+    then layer 0's four products alone, each launch on the second stream
+    beside the main stream's next layer."""
     wl, cfg, ocfg, layout, flat, batches = setup_case("small", "bf16", k=2, n_layer=5)
     print("small bf16, 5 layers, k=2", flush=True)
     _, gs = gpu_step(cfg, flat, batches)
@@ -394,7 +394,7 @@ def test_kernel_timer_counts_launches_and_leaves_results_unchanged():
 def test_kernel_timer_second_stream_and_layernorm_slots():
     """The weight-gradient timer (events on the library's second stream for
     six bf16 layers: pairs 5-4, 3-2 and 1-0; five layers: pairs 4-3 and 2-1,
-    then layer 0 alone on the main stream) and the LayerNorm timers (2 L + 1
+    then layer 0 alone, also there) and the LayerNorm timers (2 L + 1
     launches per forward and per backward) count every launch of a
     two-micro-step step and leave the result bit-identical."""
     wl, cfg, ocfg, layout, flat, batches = setup_case("small", "bf16", k=2)
@@ -540,7 +540,7 @@ def test_bf16_350m_width_four_layers_matches_oracle():
     2): the general LayerNorm kernels, the 4096-deep fc-projection product,
     and weight gradients whose two-layer group (384 tiles of 256 x 256) does
     not fit one round of the 256 CUs, so each layer's four products run as
-    one launch alone while the second stream stays unused."""
+    one launch alone, on the second stream beside the next layer's work."""
     wl, cfg, ocfg, layout, flat, batches = setup_case("gpt2_350m", "bf16", k=1, B=2, n_layer=4)
     print("bf16 gpt2_350m width: 4 layers, B=2, T=1024", flush=True)
     _, gs = gpu_step(cfg, flat, batches)
