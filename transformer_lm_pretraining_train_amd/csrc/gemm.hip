@@ -284,7 +284,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K,
 // past N).
 template <int MODE>
 __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int N, const float* v,
-                                           int split, int M, float* res) {
+                                           int split, int M, float* res,
+                                           const float* bias8 = nullptr) {
   if constexpr (MODE == EPI_PARTIAL) {
     float* o = (float*)e.out + (int64_t)split * M * N + (int64_t)m * N + n;
     if (n + 8 <= N && (N & 3) == 0) {
@@ -313,10 +314,15 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = v[j];
       if constexpr (MODE == EPI_BIAS || MODE == EPI_BIAS_RESID || MODE == EPI_BIAS_GELU) {
-        float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
-        float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
-        x[0] += b0.x; x[1] += b0.y; x[2] += b0.z; x[3] += b0.w;
-        x[4] += b1.x; x[5] += b1.y; x[6] += b1.z; x[7] += b1.w;
+        if (bias8) {  // bias[n .. n+7], loaded by the caller
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] += bias8[j];
+        } else {
+          float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
+          float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
+          x[0] += b0.x; x[1] += b0.y; x[2] += b0.z; x[3] += b0.w;
+          x[4] += b1.x; x[5] += b1.y; x[6] += b1.z; x[7] += b1.w;
+        }
       }
       if constexpr (MODE == EPI_BIAS_RESID) {
         Pack<bf16> r = load_pack((const bf16*)e.resid + (int64_t)m * e.ldr + n);
@@ -360,6 +366,8 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
     }
   }
 }
+
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int chunk) { return r * 64 + ((chunk ^ swz(r)) << 3); }
@@ -747,6 +755,39 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
     s1 = sbig + ssmall * fast_exp(small - big);
     m1 = big;
   };
+  // Bias of the columns this lane stores: lane c handles the 8-column
+  // chunks (c + 64 t) % CPRW of each slab row, which cycle through only
+  // NBD = CPRW / gcd(64, CPRW) values, so the lane loads those once per tile
+  // instead of once per stored chunk (the loads would share the address path
+  // with the stores).  Done for the 192-wide tiles (three chunks per lane,
+  // one column round); the 256-wide ones would need one register more than
+  // they have.
+  constexpr int CPRW = JB * 4;        // 8-column chunks per slab row
+  constexpr int CHUNKS = 32 * CPRW;   // chunks in the slab
+  static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
+  constexpr int NBD = CPRW / gcd_c(64, CPRW);
+  static_assert(JB != 3 || NBD == 3, "12 chunks per row: three per lane");
+  static_assert(JB != 2 || NBD == 1, "8 chunks per row: one per lane");
+  constexpr bool kBiasPre =
+      (MODE == EPI_BIAS || MODE == EPI_BIAS_RESID || MODE == EPI_BIAS_GELU) && JB == 3;
+  float bpre[kBiasPre ? TJ / JB : 1][kBiasPre ? NBD : 1][8];
+  if constexpr (kBiasPre) {
+#pragma unroll
+    for (int jr = 0; jr < TJ / JB; ++jr)
+#pragma unroll
+      for (int d = 0; d < NBD; ++d) {
+        const int n = n0 + wn * WN + jr * JB * 32 + ((lane + 64 * d) % CPRW) * 8;
+        if (n + 8 <= N) {
+          const float4 b0 = *reinterpret_cast<const float4*>(e.bias + n);
+          const float4 b1 = *reinterpret_cast<const float4*>(e.bias + n + 4);
+          bpre[jr][d][0] = b0.x; bpre[jr][d][1] = b0.y; bpre[jr][d][2] = b0.z; bpre[jr][d][3] = b0.w;
+          bpre[jr][d][4] = b1.x; bpre[jr][d][5] = b1.y; bpre[jr][d][6] = b1.z; bpre[jr][d][7] = b1.w;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bpre[jr][d][j] = 0.f;  // unused: the ragged edge reads e.bias
+        }
+      }
+  }
   constexpr bool kColsum = MODE == EPI_GELU_BWD;
   static_assert(!kColsum || WM == 64, "colsum blocks are the waves' 64 rows");
   const bool colsum = kColsum && e.colsum != nullptr;
@@ -774,9 +815,6 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
               make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
         }
       __builtin_amdgcn_wave_barrier();
-      constexpr int CPRW = JB * 4;        // 8-column chunks per slab row
-      constexpr int CHUNKS = 32 * CPRW;   // chunks in the slab
-      static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
 #pragma unroll
       for (int t = 0; t < CHUNKS / 64; ++t) {
         const int c = lane + 64 * t;
@@ -807,7 +845,13 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
           continue;
         }
         float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (m < M && n < N) epi_apply8<MODE>(e, m, n, N, v, split, M, res);
+        if (m < M && n < N) {
+          if constexpr (kBiasPre) {
+            epi_apply8<MODE>(e, m, n, N, v, split, M, res, bpre[jr][t % NBD]);
+          } else {
+            epi_apply8<MODE>(e, m, n, N, v, split, M, res);
+          }
+        }
         if (colsum) {  // this lane alone read these slab entries
           *reinterpret_cast<float4*>(slab + row * SP + col) = make_float4(res[0], res[1], res[2], res[3]);
           *reinterpret_cast<float4*>(slab + row * SP + col + 4) = make_float4(res[4], res[5], res[6], res[7]);
