@@ -112,6 +112,47 @@ def test_gemm_epilogues(dt, epi):
         assert rel_l2(r["got2"], r["expect2"]) < (1e-5 if dt == FP32 else 4e-3)
 
 
+@pytest.mark.parametrize("epi", ["bias", "bias_resid", "bias_gelu"])
+@pytest.mark.parametrize("N,ldo", [(520, 520), (514, 520)])
+def test_bias_epilogues_on_192_wide_tiles(epi, N, ldo):
+    """The bias epilogues on the 256 x 192 large-tile kernel (the qkv, fc and
+    projection products of the model; M = 16384 rows make three 192-wide tile
+    columns the cheapest plan for these N), where each lane loads its bias
+    once per tile: a last tile column 136 or 130 wide, and for N = 514 a
+    last 8-column chunk that reaches past N (element-wise there, 16-byte
+    accesses elsewhere, output pitch 520).  All outputs against fp64 of the
+    bf16-rounded inputs."""
+    M, K = 16384, 136
+    print(f"gemm 256x192 {epi} N={N} ldo={ldo}", flush=True)
+    rng = np.random.default_rng(N + len(epi))
+    A = bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    B = bf16_round(rng.standard_normal((N, K)).astype(np.float32))
+    bias = rng.standard_normal(N).astype(np.float32)
+    resid = bf16_round(rng.standard_normal((M, ldo)).astype(np.float32))
+    ref = A.astype(np.float64) @ B.astype(np.float64).T + bias
+    if epi == "bias_resid":
+        ref = ref + resid[:, :N]
+    out = torch.full((M, ldo), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kw = {"bias": to_dev(bias)}
+    if epi == "bias_resid":
+        kw.update(resid=to_dev(resid, torch.bfloat16), ldr=ldo)
+    if epi == "bias_gelu":
+        out2 = torch.full((M, ldo), float("nan"), dtype=torch.bfloat16, device="cuda")
+        kw.update(out2=out2, ldo2=ldo)
+    g.gemm(BF16, True, True, M, N, K, to_dev(A, torch.bfloat16), K, to_dev(B, torch.bfloat16), K,
+           epi, out, ldo, **kw)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.all(np.isnan(got[:, N:])), "columns past N were written"
+    got = got[:, :N]
+    assert rel_l2(got, ref) < 4e-3
+    # the last tile column on its own (ragged edge)
+    assert rel_l2(got[:, 384:], ref[:, 384:]) < 4e-3
+    if epi == "bias_gelu":
+        g2 = host(out2)[:, :N]
+        assert rel_l2(g2, oracle.gelu(got.astype(np.float64))) < 4e-3
+
+
 @pytest.mark.parametrize("akm,bkm", ORIENT)
 @pytest.mark.parametrize("K,pad", [(200, 0), (40, 0), (136, 3)])
 def test_gemm_store_persistent_256_tiles(akm, bkm, K, pad):
