@@ -282,10 +282,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K,
 // the row pitches allow it, element-wise at the ragged right edge).
 // res[j]: the value stored to out[m, n + j] as rounded (bf16 outputs; 0
 // past N).
-template <int MODE>
+// AUXV: the 16-byte path takes the GELU backward's pre-activations from auxv
+// (loaded by the caller) instead of loading them.
+template <int MODE, bool AUXV = false>
 __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int N, const float* v,
                                            int split, int M, float* res,
-                                           const float* bias8 = nullptr) {
+                                           const float* bias8 = nullptr,
+                                           Pack<bf16> auxv = Pack<bf16>{}) {
   if constexpr (MODE == EPI_PARTIAL) {
     float* o = (float*)e.out + (int64_t)split * M * N + (int64_t)m * N + n;
     if (n + 8 <= N && (N & 3) == 0) {
@@ -341,7 +344,9 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
         }
       }
       if constexpr (MODE == EPI_GELU_BWD) {
-        Pack<bf16> h = load_pack((const bf16*)e.aux + (int64_t)m * e.ldx + n);
+        Pack<bf16> h;
+        if constexpr (AUXV) h = auxv;
+        else h = load_pack((const bf16*)e.aux + (int64_t)m * e.ldx + n);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] *= gelu_grad_f(to_f(h.e[j]));
         if (e.out2) {  // GELU(h) again, as the forward's bias + GELU epilogue stored it
@@ -375,6 +380,7 @@ __device__ __forceinline__ int lds_off(int r, int chunk) { return r * 64 + ((chu
 constexpr int BIG_THREADS = 512;  // 8 waves: 4 along M x 2 along N
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 // Buffer-resource word 3 for raw (unswizzled, stride 0) buffers on CDNA:
 // 32-bit data format, range checking against num_records.
@@ -815,6 +821,40 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
               make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
         }
       __builtin_amdgcn_wave_barrier();
+      // GELU backward: the round's pre-activations are all requested before
+      // its first store, so that waiting for one of them does not also wait
+      // for the stores of the chunks before it (one in-order counter covers
+      // loads and stores; loaded chunk by chunk, each load waited for every
+      // store before it: step 0.6 % slower)
+      constexpr bool kAuxBatch = MODE == EPI_GELU_BWD;
+      Pack<bf16> hb[kAuxBatch ? CHUNKS / 64 : 1];
+      if constexpr (kAuxBatch) {
+        // buffer loads without branches: a chunk that is not stored from
+        // these registers carries an out-of-range offset and reads zeros
+        const bool vec = (e.ldo & 7) == 0 && (e.ldr & 7) == 0 && (e.ldo2 & 7) == 0 && (e.ldx & 7) == 0;
+        const int r0 = m0 + wm * WM + i * 32;  // the round's first row
+        const int rows = min(M - r0, 32);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const bf16*)e.aux + (int64_t)r0 * e.ldx), (short)0,
+            rows > 0 ? (int)((int64_t)rows * e.ldx * 2) : 0, (int)kRsrcWord3);
+#pragma unroll
+        for (int t = 0; t < CHUNKS / 64; ++t) {
+          const int c = lane + 64 * t;
+          const int r = c / CPRW;
+          const int n = n0 + wn * WN + jr * JB * 32 + (c % CPRW) * 8;
+          // exactly the chunks epi_apply8 stores on its 16-byte path
+          const bool ok = vec && r < rows && n + 8 <= N;
+          const uint32_t off = ok ? (uint32_t)(((int64_t)r * e.ldx + n) * 2) : kOOB;
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist only for the GPU target
+          const v4u32 w = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+          hb[t].u = make_uint4(w.x, w.y, w.z, w.w);
+#else
+          (void)rs;
+          (void)off;
+          hb[t].u = make_uint4(0, 0, 0, 0);
+#endif
+        }
+      }
 #pragma unroll
       for (int t = 0; t < CHUNKS / 64; ++t) {
         const int c = lane + 64 * t;
@@ -848,6 +888,8 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         if (m < M && n < N) {
           if constexpr (kBiasPre) {
             epi_apply8<MODE>(e, m, n, N, v, split, M, res, bpre[jr][t % NBD]);
+          } else if constexpr (kAuxBatch) {
+            epi_apply8<MODE, true>(e, m, n, N, v, split, M, res, nullptr, hb[t]);
           } else {
             epi_apply8<MODE>(e, m, n, N, v, split, M, res);
           }
