@@ -282,8 +282,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(int M, int N, int K,
 // the row pitches allow it, element-wise at the ragged right edge).
 // res[j]: the value stored to out[m, n + j] as rounded (bf16 outputs; 0
 // past N).
-// AUXV: the 16-byte path takes the GELU backward's pre-activations from auxv
-// (loaded by the caller) instead of loading them.
+// AUXV: the 16-byte path takes the GELU backward's pre-activations, or the
+// residual, from auxv (loaded by the caller) instead of loading them.
 template <int MODE, bool AUXV = false>
 __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int N, const float* v,
                                            int split, int M, float* res,
@@ -328,7 +328,9 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
         }
       }
       if constexpr (MODE == EPI_BIAS_RESID) {
-        Pack<bf16> r = load_pack((const bf16*)e.resid + (int64_t)m * e.ldr + n);
+        Pack<bf16> r;
+        if constexpr (AUXV) r = auxv;
+        else r = load_pack((const bf16*)e.resid + (int64_t)m * e.ldr + n);
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] += to_f(r.e[j]);
       }
@@ -821,12 +823,15 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
               make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
         }
       __builtin_amdgcn_wave_barrier();
-      // GELU backward: the round's pre-activations are all requested before
-      // its first store, so that waiting for one of them does not also wait
-      // for the stores of the chunks before it (one in-order counter covers
-      // loads and stores; loaded chunk by chunk, each load waited for every
-      // store before it: step 0.6 % slower)
-      constexpr bool kAuxBatch = MODE == EPI_GELU_BWD;
+      // GELU backward and bias + residual: the round's pre-activations (or
+      // residual rows) are all requested before its first store, so that
+      // waiting for one of them does not also wait for the stores of the
+      // chunks before it (one in-order counter covers loads and stores;
+      // loaded chunk by chunk, each load waited for every store before it:
+      // step 0.6 % and 0.3 % slower)
+      constexpr bool kAuxBatch = MODE == EPI_GELU_BWD || MODE == EPI_BIAS_RESID;
+      const bf16* const asrc = (const bf16*)(MODE == EPI_GELU_BWD ? e.aux : e.resid);
+      const int64_t ald = MODE == EPI_GELU_BWD ? e.ldx : e.ldr;
       Pack<bf16> hb[kAuxBatch ? CHUNKS / 64 : 1];
       if constexpr (kAuxBatch) {
         // buffer loads without branches: a chunk that is not stored from
@@ -835,8 +840,8 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         const int r0 = m0 + wm * WM + i * 32;  // the round's first row
         const int rows = min(M - r0, 32);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const bf16*)e.aux + (int64_t)r0 * e.ldx), (short)0,
-            rows > 0 ? (int)((int64_t)rows * e.ldx * 2) : 0, (int)kRsrcWord3);
+            (void*)(asrc + (int64_t)r0 * ald), (short)0, rows > 0 ? (int)((int64_t)rows * ald * 2) : 0,
+            (int)kRsrcWord3);
 #pragma unroll
         for (int t = 0; t < CHUNKS / 64; ++t) {
           const int c = lane + 64 * t;
@@ -844,7 +849,7 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
           const int n = n0 + wn * WN + jr * JB * 32 + (c % CPRW) * 8;
           // exactly the chunks epi_apply8 stores on its 16-byte path
           const bool ok = vec && r < rows && n + 8 <= N;
-          const uint32_t off = ok ? (uint32_t)(((int64_t)r * e.ldx + n) * 2) : kOOB;
+          const uint32_t off = ok ? (uint32_t)(((int64_t)r * ald + n) * 2) : kOOB;
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer builtins exist only for the GPU target
           const v4u32 w = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
           hb[t].u = make_uint4(w.x, w.y, w.z, w.w);
@@ -886,7 +891,9 @@ __global__ __launch_bounds__(BigWaves<BN>::NW * 64) void gemm_big_kernel(const B
         }
         float res[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (m < M && n < N) {
-          if constexpr (kBiasPre) {
+          if constexpr (kBiasPre && kAuxBatch) {
+            epi_apply8<MODE, true>(e, m, n, N, v, split, M, res, bpre[jr][t % NBD], hb[t]);
+          } else if constexpr (kBiasPre) {
             epi_apply8<MODE>(e, m, n, N, v, split, M, res, bpre[jr][t % NBD]);
           } else if constexpr (kAuxBatch) {
             epi_apply8<MODE, true>(e, m, n, N, v, split, M, res, nullptr, hb[t]);
