@@ -404,21 +404,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < 8; ++i) dwacc[j][i] = dbacc[j][i] = doacc[j][i] = 0.f;
 
-  auto fetch = [&](int row, Raw8<T> (&x)[NC], Raw8<T> (&g)[NC], Raw8<T> (&d)[NC]) {
-    if (row < M) {
+  // Branch-free loads through buffer resources: a row past M (and d res
+  // when not accumulating: an empty resource) reads zeros, so the compiler
+  // can count the loads in flight and wait only for the row it processes
+  // (loaded inside branches, every row waited for the next row's prefetch
+  // as well).
+  const int nbytes = M * C * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)inp, (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc((void*)dy, (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)dres_in, (short)0, accumulate ? nbytes : 0, 0x00020000);
+  auto bload = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t off, Raw8<T>& r) {
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const int64_t off = (int64_t)row * C + (l + 32 * j) * 8;
-        load_raw(inp + off, x[j]);
-        load_raw(dy + off, g[j]);
-        if (accumulate) load_raw(dres_in + off, d[j]);
-      }
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) {
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0);
+      r.u[i] = make_uint4(w.x, w.y, w.z, w.w);
+    }
+#else
+    (void)rs;
+    (void)off;
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.u[i] = make_uint4(0, 0, 0, 0);
+#endif
+  };
+  auto fetch = [&](int row, Raw8<T> (&x)[NC], Raw8<T> (&g)[NC], Raw8<T> (&d)[NC]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const uint32_t off = row < M ? (uint32_t)(((int64_t)row * C + (l + 32 * j) * 8) * sizeof(T))
+                                   : 0x80000000u;
+      bload(rx, off, x[j]);
+      bload(rg, off, g[j]);
+      bload(rd, off, d[j]);
     }
   };
   auto process = [&](int row, const Raw8<T> (&x)[NC], const Raw8<T> (&g)[NC],
-                     const Raw8<T> (&d)[NC]) {
+                     const Raw8<T> (&d)[NC], float mu, float rs) {
     if (row >= M) return;  // uniform over the half-wave; its sums stay inside it
-    const float mu = mean[row], rs = rstd[row];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -456,13 +478,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int r0 = blockIdx.x * LNB_ROWS + hw;
   constexpr int RPH = LNB_ROWS / 8;  // rows per half-wave
+  // every row's mean and rstd first, so that waiting for them never waits
+  // for a later row's prefetch (one in-order counter for all loads)
+  float mus[RPH], rss[RPH];
+#pragma unroll
+  for (int i = 0; i < RPH; ++i) {
+    const int rr = min(r0 + 8 * i, M - 1);
+    mus[i] = mean[rr];
+    rss[i] = rstd[rr];
+  }
   Raw8<T> xa[NC], ga[NC], da[NC];
   fetch(r0, xa, ga, da);
-#pragma unroll 1
+#pragma unroll
   for (int i = 0; i < RPH; ++i) {
     Raw8<T> xb[NC], gb[NC], db[NC];
     if (i + 1 < RPH) fetch(r0 + 8 * (i + 1), xb, gb, db);
-    process(r0 + 8 * i, xa, ga, da);
+    process(r0 + 8 * i, xa, ga, da, mus[i], rss[i]);
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       xa[j] = xb[j];
@@ -596,8 +627,15 @@ hipError_t layernorm_backward(int dt, void* dres, const void* dres_in, float* dw
   layernorm_bwd_hw_kernel<T, NC><<<nb, 256, 0, s>>>(                                           \
       (T*)dres, (const T*)(dres_in ? dres_in : dres), partial, (const T*)dy, (const T*)inp, mean, \
       rstd, w, M, C, accumulate ? 1 : 0)
-  // the half-wave kernel where its registers suffice: bf16 up to C = 768, fp32 up to 512
-  if (C == 256 && dt == BF16) LNBH(bf16, 1);
+  // the half-wave kernel where its registers suffice (bf16 up to C = 768,
+  // fp32 up to 512) and its 32-bit buffer ranges cover the rows
+  const bool hw_ok = (int64_t)M * C * (dt == BF16 ? 2 : 4) < ((int64_t)1 << 31);
+  if (!hw_ok) {
+    if (nch == 1) LNB(1);
+    else if (nch == 2) LNB(2);
+    else if (nch == 3) LNB(3);
+    else LNB(4);
+  } else if (C == 256 && dt == BF16) LNBH(bf16, 1);
   else if (C == 256) LNBH(float, 1);
   else if (C == 512 && dt == BF16) LNBH(bf16, 2);
   else if (C == 512) LNBH(float, 2);
