@@ -560,13 +560,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qb0 = k0w / TB, nqb = (int)cdiv(T, TB);
   TileRegs rq, rd;
   float lsv = 0.f, dsv = 0.f;
+  int lqb = 0;  // the query tile lsv and dsv belong to
   auto gload = [&](int qb) {
     tile_load(rq, qbase, ld, qb * TB, T);
     tile_load(rd, dobase, C, qb * TB, T);
-    if (threadIdx.x < TB) {
-      int q = qb * TB + threadIdx.x;
-      lsv = q < T ? lse[(int64_t)bh * T + q] * LOG2E : INFINITY;
-      dsv = q < T ? Dbuf[(int64_t)bh * T + q] : 0.f;
+    // every thread loads (from a clamped index; the first TB store them):
+    // loads inside a branch made the compiler wait for them, and with them
+    // for the tile loads just issued, right away
+    {
+      const int qc = min(qb * TB + (int)(threadIdx.x % TB), T - 1);
+      lsv = lse[(int64_t)bh * T + qc];  // raw: sstore applies q < T and the scale,
+      dsv = Dbuf[(int64_t)bh * T + qc];  // so that nothing waits for them before
+      lqb = qb;
     }
   };
   auto sstore = [&](int stage) {
@@ -574,8 +579,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     tile_store(rq, dst);
     tile_store(rd, dst + TILE);
     if (threadIdx.x < TB) {
-      LD[stage][0][threadIdx.x] = lsv;
-      LD[stage][1][threadIdx.x] = dsv;
+      const bool in = lqb * TB + (int)threadIdx.x < T;
+      LD[stage][0][threadIdx.x] = in ? lsv * LOG2E : INFINITY;
+      LD[stage][1][threadIdx.x] = in ? dsv : 0.f;
     }
   };
   // One 64-query tile for this wave's 32 keys; DIAG (compile-time) on the
