@@ -424,26 +424,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const float c = 0.125f * LOG2E;
 
   bf16x8_t qf[4], df[4];
-  const bf16* dorow = dout + ((int64_t)b * T + myq) * C + hh * HD;
-  const bf16* orow = out + ((int64_t)b * T + myq) * C + hh * HD;
-  float Dp = 0.f;
+  // Start-up loads without branches (a row past T is read from row T-1 and
+  // zeroed), with the log-sum-exp and the first K and V tiles issued before
+  // anything waits, so that one memory latency covers them all (inside
+  // branches the compiler waited after each group).
+  const int myqc = min(myq, T - 1);
+  const bf16* dorow = dout + ((int64_t)b * T + myqc) * C + hh * HD;
+  const bf16* orow = out + ((int64_t)b * T + myqc) * C + hh * HD;
+  const bf16* qrow = base + (int64_t)myqc * ld + hh * HD;
+  bf16x8_t of[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    qf[ks] = frag_global(base + (int64_t)myq * ld + hh * HD, ks, h2, qvalid);
-    df[ks] = frag_global(dorow, ks, h2, qvalid);
-    bf16x8_t of = frag_global(orow, ks, h2, qvalid);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) Dp += (float)df[ks][j] * (float)of[j];
+    qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16 + h2 * 8);
+    df[ks] = *reinterpret_cast<const bf16x8_t*>(dorow + ks * 16 + h2 * 8);
+    of[ks] = *reinterpret_cast<const bf16x8_t*>(orow + ks * 16 + h2 * 8);
   }
-  const float Dq = Dp + __shfl_xor(Dp, 32, 64);
-  const float L2 = qvalid ? lse[(int64_t)bh * T + myq] * LOG2E : 0.f;
-  if (qvalid && h2 == 0) Dbuf[(int64_t)bh * T + myq] = Dq;
-
-  f32x16_t dq[2] = {zero16(), zero16()};
+  const float lsraw = lse[(int64_t)bh * T + myqc];
   const int nkb = (int)min(cdiv(q0 + WQ, TB), cdiv(T, TB));
   TileRegs rk, rv;
   tile_load(rk, kbase, ld, 0, T);
   tile_load(rv, vbase, ld, 0, T);
+  float Dp = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (!qvalid) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[ks][j] = df[ks][j] = (bf16)0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Dp += (float)df[ks][j] * (float)of[ks][j];
+  }
+  const float Dq = Dp + __shfl_xor(Dp, 32, 64);
+  const float L2 = qvalid ? lsraw * LOG2E : 0.f;
+  if (qvalid && h2 == 0) Dbuf[(int64_t)bh * T + myq] = Dq;
+  f32x16_t dq[2] = {zero16(), zero16()};
   tile_store(rk, smem);
   tile_store(rv, smem + TILE);
   if (nkb > 1) {
