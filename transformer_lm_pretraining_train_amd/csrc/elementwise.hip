@@ -900,9 +900,15 @@ __global__ __launch_bounds__(NT) void ce_fused_kernel(
   constexpr int NWV = NT / 64, STEP = NT * 8;
   __shared__ SoftmaxState part[NWV];
   __shared__ float lse_s;
-  __shared__ int y_s;
   const int row = blockIdx.x;
   const T* z = logits + (int64_t)row * ldl;
+  // The target and its logit are read before the row, so that the serial
+  // step after the reduction (one thread, the rest of the workgroup waiting
+  // at the barrier) has no memory latency left in it (the kernel was waiting
+  // for two dependent loads there per row).
+  const int y_in = targets[row];
+  const int y = y_in < 0 ? 0 : (y_in >= V ? V - 1 : y_in);  // clamped; flagged below
+  const float zy = to_f(z[y]);
   Raw8<T> r[NCHK];
 #pragma unroll
   for (int c = 0; c < NCHK; ++c) {
@@ -954,20 +960,14 @@ __global__ __launch_bounds__(NT) void ce_fused_kernel(
     SoftmaxState t = part[0];
     for (int w = 1; w < NWV; ++w) t = sm_combine(t, part[w]);
     const float lse = t.m + logf(t.s);
-    int y = targets[row];
-    if (y < 0 || y >= V) {
-      atomicOr(flag, 2);
-      y = y < 0 ? 0 : V - 1;
-    }
-    losses[row] = lse - to_f(z[y]);
+    if (y_in < 0 || y_in >= V) atomicOr(flag, 2);
+    losses[row] = lse - zy;
     lse_out[row] = lse;
     argmax_out[row] = t.arg;
     lse_s = lse;
-    y_s = y;
   }
   __syncthreads();
   const float lse = lse_s;
-  const int y = y_s;
   T* d = dz + (int64_t)row * ldl;
 #pragma unroll
   for (int c = 0; c < NCHK; ++c) {
