@@ -179,9 +179,15 @@ __device__ __forceinline__ void put_row(float* __restrict__ dst, const float acc
 // A window's C columns are split over G waves (column groups of 64 chunks
 // of 8, so that twice as many waves run at C = 768); lane l of group g owns
 // chunk 64 g + l (NCH = 1) or chunks 64 (g NCH + k) + l.  Every group sees
-// the same runs and adds in the same slot order.  Rows are fetched EB_BATCH
-// slots at a time so that that many loads are in flight, then added in slot
-// order.
+// the same runs and adds in the same slot order.  Rows are fetched EB_BATCH /
+// NCH slots at a time, and with each slot's dx row the dwte row of its token:
+// a token's slots form one run, so a run that ends in this window and lies
+// wholly inside it is the only writer of that dwte row, and reading the row
+// before the batch's stores reads what the add needs.  All of a batch's
+// loads are issued at once from valid addresses (a slot past the window or a
+// lane past the columns reads a valid row it does not use), so one memory
+// latency covers them; a read-modify-write per run end made every wave wait
+// once per slot behind its previous store.
 constexpr int EB_BATCH = 8;
 
 template <class T, int NCH>
@@ -190,6 +196,7 @@ __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ d
                                                          const int32_t* __restrict__ stok,
                                                          float* __restrict__ dwte,
                                                          float* __restrict__ part) {
+  constexpr int NB = EB_BATCH / NCH;  // slots per batch
   const int lane = threadIdx.x % 64;
   const int wg = blockIdx.x * 4 + threadIdx.x / 64;
   const int w = wg / G, g = wg % G;
@@ -204,21 +211,22 @@ __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ d
   const int next_tok = s0 + n < M ? stok[s0 + n] : -1;
   float acc[NCH][8];
   int run_first = 0;
-  for (int i0 = 0; i0 < n; i0 += EB_BATCH) {
-    float rows[EB_BATCH][NCH][8];
+  for (int i0 = 0; i0 < n; i0 += NB) {
+    float rows[NB][NCH][8], old[NB][NCH][8];
 #pragma unroll
-    for (int b = 0; b < EB_BATCH; ++b) {
-      const int i = i0 + b;
-      const int pos = __builtin_amdgcn_readlane(mypos, i < n ? i : 0);
-      const T* row = dx + (int64_t)pos * C;
+    for (int b = 0; b < NB; ++b) {
+      const int ic = min(i0 + b, n - 1);
+      const int pos = __builtin_amdgcn_readlane(mypos, ic);
+      const int t = __builtin_amdgcn_readlane(mytok, ic);
 #pragma unroll
       for (int k = 0; k < NCH; ++k) {
-        const int ch = ch0 + 64 * k;
-        if (i < n && ch < nch) load_row_chunk(row + ch * 8, rows[b][k]);
+        const int ch = min(ch0 + 64 * k, nch - 1);
+        load_row_chunk(dx + (int64_t)pos * C + ch * 8, rows[b][k]);
+        load_row_chunk(dwte + (int64_t)t * C + ch * 8, old[b][k]);
       }
     }
 #pragma unroll
-    for (int b = 0; b < EB_BATCH; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const int i = i0 + b;
       if (i >= n) break;
       const int t = __builtin_amdgcn_readlane(mytok, i);
@@ -243,8 +251,10 @@ __global__ __launch_bounds__(256) void emb_window_kernel(const T* __restrict__ d
         for (int k = 0; k < NCH; ++k) {
           const int ch = ch0 + 64 * k;
           if (ch < nch) {
-            if (direct) add_row(dst + ch * 8, acc[k]);
-            else put_row(dst + ch * 8, acc[k]);
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = direct ? old[b][k][j] + acc[k][j] : acc[k][j];
+            put_row(dst + ch * 8, v);
           }
         }
         run_first = i + 1;
