@@ -294,7 +294,8 @@ enum {
   GPT2_DBG_ACT_QKV = 4,  /* (B*T, 3C) */
   GPT2_DBG_ACT_ATTY = 5, /* (B*T, C) attention output before the projection */
   GPT2_DBG_ACT_RES2 = 6, /* (B*T, C) residual after attention */
-  GPT2_DBG_ACT_FCH = 7,  /* (B*T, 4C) fc pre-activation */
+  GPT2_DBG_ACT_FCH = 7,  /* (B*T, 4C) fc pre-activation h; with recompute 0 (GELU(h) kept)
+                            GELU'(h) instead, the only form of it the backward reads */
   GPT2_DBG_ACT_RES3 = 8, /* (B*T, C) residual after the MLP (block output) */
   GPT2_DBG_ACT_LNF = 9,  /* (B*T, C) final LayerNorm output */
   GPT2_DBG_ATT_LSE = 10, /* (B, H, T) fp32 log-sum-exp of the scaled scores */

@@ -73,11 +73,12 @@ __device__ __forceinline__ float gelu_sigmoid(float h) {
 __device__ __forceinline__ float gelu_f(float h) { return h * gelu_sigmoid(h); }
 // d gelu / d h = 0.5 (1 + t) + 0.5 h (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 h^2)
 //             = s + 2 h s (1 - s) sqrt(2/pi) (1 + 0.134145 h^2).
-__device__ __forceinline__ float gelu_grad_f(float h) {
-  const float s = gelu_sigmoid(h);
+// gelu_grad_s takes s = gelu_sigmoid(h) already computed.
+__device__ __forceinline__ float gelu_grad_s(float h, float s) {
   const float k = 2.0f * 0.7978845608028654f;
   return __builtin_fmaf(k * h * s * (1.0f - s), __builtin_fmaf(3.0f * 0.044715f * h, h, 1.0f), s);
 }
+__device__ __forceinline__ float gelu_grad_f(float h) { return gelu_grad_s(h, gelu_sigmoid(h)); }
 
 // Workgroups are dealt to the 8 XCDs of the chip round-robin by id, and each
 // XCD has its own L2.  xcd_remap turns the hardware id into a logical index

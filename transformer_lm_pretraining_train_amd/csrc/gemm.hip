@@ -50,7 +50,9 @@ __device__ __forceinline__ float epi_apply(const Epilogue& e, int m, int n, floa
     y = from_f<T>(acc + e.bias[n]);
     // GELU of the stored (rounded) pre-activation, so that the backward,
     // which differentiates at the stored value, is consistent with it.
-    ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(to_f(y)));
+    const float h = to_f(y), sg = gelu_sigmoid(h);
+    ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(h * sg);
+    if (e.dgelu) y = from_f<T>(gelu_grad_s(h, sg));  // GELU'(h) in place of h
   } else if constexpr (MODE == EPI_DLOGITS) {
     const int c = e.col0 + n;
     const int yy = min(max(e.targets[m], 0), e.vocab - 1);
@@ -58,10 +60,14 @@ __device__ __forceinline__ float epi_apply(const Epilogue& e, int m, int n, floa
     if (c == yy) p -= 1.f;
     y = from_f<T>(p * e.scale);
   } else if constexpr (MODE == EPI_GELU_BWD) {
-    float h = to_f(((const T*)e.aux)[(int64_t)m * e.ldx + n]);
-    y = from_f<T>(acc * gelu_grad_f(h));
-    // out2 (optional): GELU(h) again, as the forward's bias + GELU epilogue stored it
-    if (e.out2) ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(h));
+    const float a = to_f(((const T*)e.aux)[(int64_t)m * e.ldx + n]);
+    if (e.dgelu) {  // aux: GELU'(h) as the forward stored it
+      y = from_f<T>(acc * a);
+    } else {  // aux: h; GELU'(h) rounded as the forward would store it
+      y = from_f<T>(acc * to_f(from_f<T>(gelu_grad_f(a))));
+      // out2 (optional): GELU(h) again, as the forward's bias + GELU epilogue stored it
+      if (e.out2) ((T*)e.out2)[(int64_t)m * e.ldo2 + n] = from_f<T>(gelu_f(a));
+    }
   } else {  // EPI_ACC_F32
     float* of = (float*)e.out + (int64_t)m * e.ldo + n;
     *of += acc;
@@ -349,13 +355,18 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
         Pack<bf16> h;
         if constexpr (AUXV) h = auxv;
         else h = load_pack((const bf16*)e.aux + (int64_t)m * e.ldx + n);
+        if (e.dgelu) {  // h holds GELU'(pre-activation), as the forward stored it
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] *= gelu_grad_f(to_f(h.e[j]));
-        if (e.out2) {  // GELU(h) again, as the forward's bias + GELU epilogue stored it
-          Pack<bf16> g2;
+          for (int j = 0; j < 8; ++j) x[j] *= to_f(h.e[j]);
+        } else {  // GELU' of h, rounded as the forward would store it
 #pragma unroll
-          for (int j = 0; j < 8; ++j) g2.e[j] = (bf16)gelu_f(to_f(h.e[j]));
-          store_pack((bf16*)e.out2 + (int64_t)m * e.ldo2 + n, g2);
+          for (int j = 0; j < 8; ++j) x[j] *= (float)(bf16)gelu_grad_f(to_f(h.e[j]));
+          if (e.out2) {  // GELU(h) again, as the forward's bias + GELU epilogue stored it
+            Pack<bf16> g2;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) g2.e[j] = (bf16)gelu_f(to_f(h.e[j]));
+            store_pack((bf16*)e.out2 + (int64_t)m * e.ldo2 + n, g2);
+          }
         }
       }
       Pack<bf16> o;
@@ -363,12 +374,25 @@ __device__ __forceinline__ void epi_apply8(const Epilogue& e, int m, int n, int 
       for (int j = 0; j < 8; ++j) o.e[j] = (bf16)x[j];
 #pragma unroll
       for (int j = 0; j < 8; ++j) res[j] = to_f(o.e[j]);
-      store_pack((bf16*)e.out + (int64_t)m * e.ldo + n, o);
       if constexpr (MODE == EPI_BIAS_GELU) {
-        Pack<bf16> g2;
+        // GELU of the stored pre-activation, and with dgelu its derivative
+        // (stored in its place) from the same sigmoid
+        Pack<bf16> g2, so = o;
+        if (e.dgelu) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) g2.e[j] = (bf16)gelu_f(to_f(o.e[j]));
+          for (int j = 0; j < 8; ++j) {
+            const float h = to_f(o.e[j]), sg = gelu_sigmoid(h);
+            g2.e[j] = (bf16)(h * sg);
+            so.e[j] = (bf16)gelu_grad_s(h, sg);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) g2.e[j] = (bf16)gelu_f(to_f(o.e[j]));
+        }
+        store_pack((bf16*)e.out + (int64_t)m * e.ldo + n, so);
         store_pack((bf16*)e.out2 + (int64_t)m * e.ldo2 + n, g2);
+      } else {
+        store_pack((bf16*)e.out + (int64_t)m * e.ldo + n, o);
       }
     }
   }

@@ -127,6 +127,13 @@ struct Epilogue {
   // order.
   float* colsum;
   int64_t ldcs;
+  // GELU derivative stored instead of the pre-activation.  EPI_BIAS_GELU: out
+  // receives GELU'(h) of the stored (rounded) pre-activation h in place of h
+  // (out2 still GELU(h)).  EPI_GELU_BWD: aux holds that GELU'(h), and out =
+  // acc * aux; out2 must be null.  Without the flag EPI_GELU_BWD rounds its
+  // GELU'(aux) to the element type before multiplying, so that both ways
+  // give the same bits.
+  int dgelu;
   // EPI_DLOGITS only: column n of the product is vocabulary entry col0 + n.
   const float* lse;
   const int32_t* targets;
