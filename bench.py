@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 # what the same counter reads for a plain device copy of known size.  Valid
 # only for the GEMM source it was measured on (first 16 hex digits of its
 # sha256); None until measured.  Source: profiles/gpt2_124m_bf16_train_step_counters.md.
-WGRAD_TRAFFIC = {"gemm_source_sha256_16": "3dbbe19458cdc521", "shape": [16384, 768], "fetch_kib": 519320.9,
+WGRAD_TRAFFIC = {"gemm_source_sha256_16": "8e7ff5b44e7aa6a9", "shape": [16384, 768], "fetch_kib": 519386.3,
                  "write_kib": 55296.0, "fetch_factor": 2.0, "write_factor": 1.0}
 
 
