@@ -65,18 +65,23 @@ __device__ __forceinline__ float tanh_from_exp(float u) {
 
 // GELU, tanh form: 0.5 h (1 + tanh(u)), u = sqrt(2/pi) (h + 0.044715 h^3).
 // With s = 1 / (1 + exp(-2u)) = (1 + tanh(u)) / 2 this is h s.
+// h^2 is formed once, so that the derivative below can reuse it.
 __device__ __forceinline__ float gelu_sigmoid(float h) {
   const float k2 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
-  const float u2 = k2 * h * __builtin_fmaf(0.044715f * h, h, 1.0f);
+  const float u2 = k2 * h * __builtin_fmaf(0.044715f, h * h, 1.0f);
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u2));
 }
 __device__ __forceinline__ float gelu_f(float h) { return h * gelu_sigmoid(h); }
 // d gelu / d h = 0.5 (1 + t) + 0.5 h (1 - t^2) sqrt(2/pi) (1 + 3 * 0.044715 h^2)
-//             = s + 2 h s (1 - s) sqrt(2/pi) (1 + 0.134145 h^2).
-// gelu_grad_s takes s = gelu_sigmoid(h) already computed.
+//             = s + h s (1 - s) k (1 + 0.134145 h^2),  k = 2 sqrt(2/pi).
+// gelu_grad_s takes s = gelu_sigmoid(h) already computed: four operations
+// (s (1 - s) as one fused multiply-add, h^2 shared with the sigmoid), as the
+// fc product's epilogue evaluates it for every element while the matrix
+// cores wait.
 __device__ __forceinline__ float gelu_grad_s(float h, float s) {
   const float k = 2.0f * 0.7978845608028654f;
-  return __builtin_fmaf(k * h * s * (1.0f - s), __builtin_fmaf(3.0f * 0.044715f * h, h, 1.0f), s);
+  const float q = __builtin_fmaf(k * 3.0f * 0.044715f, h * h, k);  // k (1 + 0.134145 h^2)
+  return __builtin_fmaf(__builtin_fmaf(-s, s, s) * q, h, s);
 }
 __device__ __forceinline__ float gelu_grad_f(float h) { return gelu_grad_s(h, gelu_sigmoid(h)); }
 
