@@ -25,8 +25,10 @@ enum {
   GPT2K_EPI_BIAS = 1,       /* out = acc + bias[n] */
   GPT2K_EPI_BIAS_RESID = 2, /* out = acc + bias[n] + resid[m, n] */
   GPT2K_EPI_BIAS_GELU = 3,  /* out = acc + bias[n]; out2 = gelu_tanh(out) */
-  GPT2K_EPI_GELU_BWD = 4,   /* out = acc * gelu_tanh'(aux[m, n]); if dev_out2 is not NULL
-                               also out2 = gelu_tanh(aux[m, n]) (the activation recompute) */
+  GPT2K_EPI_GELU_BWD = 4,   /* out = acc * gelu_tanh'(aux[m, n]), the derivative rounded to
+                               `dtype` first (as the model's forward stores it when it keeps
+                               the GELU output); if dev_out2 is not NULL also
+                               out2 = gelu_tanh(aux[m, n]) (the activation recompute) */
   GPT2K_EPI_ACC_F32 = 5     /* out (always fp32) += acc */
 };
 

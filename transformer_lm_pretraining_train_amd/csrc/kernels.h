@@ -102,8 +102,9 @@ enum EpiMode {
   EPI_STORE = 0,       // out = acc
   EPI_BIAS = 1,        // out = acc + bias[n]
   EPI_BIAS_RESID = 2,  // out = acc + bias[n] + resid[m, n]
-  EPI_BIAS_GELU = 3,   // out = acc + bias[n]; out2 = gelu(out)
-  EPI_GELU_BWD = 4,    // out = acc * gelu'(aux[m, n]); out2 (if not null) = gelu(aux[m, n])
+  EPI_BIAS_GELU = 3,   // out = acc + bias[n]; out2 = gelu(out); with dgelu out = gelu'(that)
+  EPI_GELU_BWD = 4,    // out = acc * T(gelu'(aux[m, n])); out2 (if not null) = gelu(aux[m, n]);
+                       // with dgelu aux holds gelu' already: out = acc * aux[m, n]
   EPI_ACC_F32 = 5,     // out (fp32) += acc
   EPI_PARTIAL = 6,     // internal: split-K partial tile, fp32
   EPI_ROWSTATS = 7,    // internal: softmax row statistics, see gemm_rowstats()
