@@ -334,6 +334,42 @@ def test_out_of_range_token_is_reported():
     m.sync()  # the flag was cleared
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_out_of_range_target_is_reported_and_clamped(dtype):
+    """A target outside [0, V) (one past the padded columns, one negative)
+    is reported as ETOKEN by the next sync and clamped: the per-position
+    losses and the gradients equal, bit for bit, those of the same step with
+    the targets clamped beforehand.  The fused cross-entropy reads the target
+    and its logit before the row; this covers that read for both ends."""
+    import torch
+    wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", dtype)
+    x, y = batches[0]
+    V = cfg.vocab_size
+    bad = y.copy()
+    bad.flat[3] = cfg.padded_vocab_size + 7
+    bad.flat[5] = -2
+    ok = np.clip(bad, 0, V - 1).astype(y.dtype)
+    print(f"{dtype} targets {bad.flat[3]}, {bad.flat[5]} against clamped", flush=True)
+    out = []
+    for yy, expect_err in ((bad, True), (ok, False)):
+        m = g.Model(cfg)
+        m.set_params(to_dev(flat))
+        m.zero_grad()
+        pl = torch.zeros(x.size, device="cuda")
+        m.forward(to_dev(x), to_dev(yy), None)
+        m.debug_read("losses", pl)
+        if expect_err:
+            with pytest.raises(g.GPT2Error) as ei:
+                m.sync()
+            assert ei.value.name == "ETOKEN"
+        m.backward()
+        m.sync()  # the flag was cleared (and the clamped run raises nothing)
+        out.append((host(pl), host(m.get_grads())))
+        m.close()
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1], out[1][1])
+
+
 def test_nonfinite_gradient_skips_update():
     wl, cfg, ocfg, layout, flat, batches = setup_case("tiny", "fp32")
     m = g.Model(cfg)
